@@ -1,0 +1,95 @@
+"""Planted mistakes in the oracle must be caught by the pins.
+
+Each mutant replaces one oracle function with a plausible wrong variant (a
+dropped ReLU, a wrong head index, an off-by-one causal prefix, a reversed
+tie rule, ...).  For every mutant at least one pin of
+``test_oracle_pins`` has to fail; a mutant that passes all pins would mean
+the pins cannot tell that mistake from the right answer.
+"""
+import numpy as np
+import pytest
+
+import oracle.indexer as oi
+from tests import test_oracle_pins as pins
+
+_orig_scores = oi.indexer_scores
+_orig_select = oi.select_topk
+_orig_dequant = oi.dequant
+
+
+def _scores_with(fn):
+    def f(qh, w, kh):
+        qh = np.asarray(qh, dtype=np.float64)
+        w = np.asarray(w, dtype=np.float64)
+        kh = np.asarray(kh, dtype=np.float64)
+        x = kh @ qh.T
+        A = (np.abs(kh) @ np.abs(qh).T) @ np.abs(w)
+        return fn(x, w), A
+    return f
+
+
+def _select_with(order_fn):
+    def f(o, k):
+        o = np.asarray(o, dtype=np.float64)
+        n = o.shape[0]
+        order = order_fn(o, np.arange(n))
+        chosen = np.sort(order[:min(k, n)])
+        idx = np.full(k, -1, dtype=np.int64)
+        sc = np.full(k, -np.inf)
+        idx[:len(chosen)] = chosen
+        sc[:len(chosen)] = o[chosen]
+        return idx, sc
+    return f
+
+
+def _prefix_short(qh, w, kh):
+    # drops the diagonal key: scores only s < t (the last key is lost)
+    kh = np.asarray(kh)
+    o, A = _orig_scores(qh, w, kh)
+    if len(o) > 1:
+        o = o.copy()
+        o[-1] = -1e30
+    return o, A
+
+
+def _no_scale_dequant(codes, scale, fmt):
+    return _orig_dequant(codes, None, fmt)
+
+
+MUTANTS = {
+    "no_relu": ("indexer_scores", _scores_with(lambda x, w: x @ w)),
+    "abs_instead_of_relu": ("indexer_scores", _scores_with(lambda x, w: np.abs(x) @ w)),
+    "relu_after_weight": ("indexer_scores", _scores_with(lambda x, w: np.maximum(x * w, 0).sum(1))),
+    "heads_reversed_in_w": ("indexer_scores", _scores_with(lambda x, w: np.maximum(x, 0) @ w[::-1])),
+    "min_instead_of_max": ("indexer_scores", _scores_with(lambda x, w: np.minimum(x, 0) @ w)),
+    "diagonal_dropped": ("indexer_scores", _prefix_short),
+    "ties_to_higher_index": ("select_topk", _select_with(lambda o, s: np.lexsort((-s, -o)))),
+    "keeps_smallest": ("select_topk", _select_with(lambda o, s: np.lexsort((s, o)))),
+    "scales_ignored": ("dequant", _no_scale_dequant),
+}
+
+PINS = [
+    lambda: pins.test_hand_example_scores_and_sets("bf16"),
+    lambda: pins.test_hand_example_scores_and_sets("fp8"),
+    pins.test_hand_example_fs_and_overlap,
+    lambda: pins.test_selection_closed_forms(5),
+    pins.test_selection_brute_force_all_k,
+    pins.test_relu_identity_linear_part,
+    pins.test_relu_gate_nonnegative_with_nonnegative_weights,
+    pins.test_single_head_unit_weight_is_relu_gemv,
+    pins.test_head_permutation_invariance,
+    pins.test_positive_scaling_equivariance,
+]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(oi, attr, fn)
+    caught = 0
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            caught += 1
+    assert caught > 0, f"no pin detects mutant {name}"
