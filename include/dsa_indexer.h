@@ -1,0 +1,193 @@
+/*
+ * dsa_indexer.h -- C ABI of the gfx950 (MI355X) lightning-indexer library.
+ *
+ * The library computes the DeepSeek Sparse Attention lightning indexer, its
+ * per-query top-k selection, the IndexCache Full/Shared layer schedule that
+ * reuses the selected indices, and the cross-layer overlap statistic.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [IC]  "IndexCache deep-dive report" (zako-mio.github.io, IndexShare 03):
+ *        abstract and section 1.1 -- the indexer is a multi-head ReLU-gated
+ *        dot product run in FP8 that scores all earlier tokens and keeps the
+ *        top k = 2048; section 1.2 -- overlap |T_i ∩ T_j| / k; section 2.1 --
+ *        F layers run the indexer and write the index cache, S layers reuse
+ *        the nearest earlier F layer's indices, the first layer is always F.
+ *  [BA]  "IndexCache" news article (hub.baai.ac.cn/view/53293), figure on the
+ *        inference loop -- the cache is one temporary index tensor that every
+ *        F layer overwrites, with no memory beyond what DSA already holds.
+ *  [IS]  "Index Share logic" tech note (foosynaptic.github.io), sections 2 and
+ *        4.2 -- per layer: indexer, top-k, sparse attention; an S layer takes
+ *        cached_indices = the last F layer's indices.
+ *  [ML]  "Multi-layer Indexer" abstract (equalang.com) -- at decode the
+ *        indexer scores the whole cache and keeps the k = 2048 best.
+ *
+ * The score of query t against key s is
+ *     score(t, s) = k_scale[s] * sum_h w[t,h] * q_scale[t,h] * ReLU(q[t,h] . k[s])
+ * with one key vector per token shared by all heads (the pages print no
+ * equation; this is the multi-head ReLU-gated dot product of [IC] 1.1).
+ * The selection keeps the min(k, n) best keys under the total order "score
+ * descending, then key index ascending" (ties go to the lower index) and
+ * returns them in ascending key order, padded with -1 (score -inf).
+ *
+ * Conventions for every entry point:
+ *  - All tensors are caller-owned device memory, row-major and contiguous.
+ *    The library allocates nothing and keeps no state between calls except a
+ *    thread-local error string.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) unless stated otherwise.  Arguments are validated on the host
+ *    before anything is enqueued; on an error nothing is enqueued and the
+ *    status says why (dsa_last_error() has the message).
+ *  - e4m3 is the OCP 8-bit float E4M3 ("e4m3fn": bias 7, max 448, no inf,
+ *    S.1111.111 = NaN); bf16 is the top half of an IEEE float32.  Inputs must
+ *    be finite.
+ *  - q, k and the decode cache must be 16-byte aligned.
+ *  - Identical inputs give identical output bytes (deterministic).
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misaligned pointer, bad pattern */
+  DSA_ERR_UNSUPPORTED = 2,   /* shape the kernels are not built for */
+  DSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query says */
+  DSA_ERR_HIP = 4            /* a HIP call failed; the message has the HIP error */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_BF16 = 0,
+  DSA_FP8_E4M3 = 1
+} dsa_dtype;
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+/* ABI revision of this header (bumped on any signature change). */
+int dsa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Prefill: one sequence of L tokens, causal, query t scores keys 0..t
+ * (diagonal included).  [IC] abstract and 1.1.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes dsa_indexer_topk_prefill needs for these sizes on the
+ * current HIP device. */
+dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa_dtype dt,
+                                              size_t* bytes);
+
+/*
+ * q        [L, H, D] dt          query heads (e4m3 codes or bf16)
+ * q_scale  fp32 or NULL (= 1)    element (t, h) at q_scale[t*(stride? H:1) + h*stride]:
+ *                                q_scale_head_stride 0 = one scale per token ([L]),
+ *                                1 = one per (token, head) ([L, H])
+ * k        [L, D] dt             keys, one vector per token shared by all heads
+ * k_scale  [L] fp32 or NULL (= 1)
+ * w        [L, H] bf16           head weights
+ * L >= 1; H in {8, 16, 32, 64}; D in {64, 128} (bf16: not H=64 with D=128);
+ * 1 <= topk <= 4096.
+ * out_idx        [L, topk] int32  selected keys, ascending, -1 padded (written in full)
+ * out_topk_score [L, topk] fp32   scores aligned with out_idx, -inf padded; NULL to skip
+ * out_dense_score [L, L] fp32     every score, -inf above the diagonal; NULL to skip;
+ *                                 only for L <= 16384 (a debugging aid: the normal path
+ *                                 never stores the L x L matrix)
+ * workspace      device bytes, at least what the query above returns; its
+ *                contents on entry do not matter.
+ * Outputs must not alias inputs.
+ */
+dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t q_scale_head_stride,
+                                    const void* k, const float* k_scale, const uint16_t* w,
+                                    int L, int H, int D, int topk, dsa_dtype dt,
+                                    int32_t* out_idx, float* out_topk_score, float* out_dense_score,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode: B sequences with one new query each, at position len_b - 1, whose
+ * own key is already in the cache; the query scores the whole cache
+ * (keys 0 .. len_b - 1).  [ML] abstract; [IS] section 2 (the indexer runs
+ * per layer at every decode step).
+ * ------------------------------------------------------------------------ */
+
+dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int topk, size_t* bytes);
+
+/*
+ * q        [B, H, D] bf16        one query per sequence
+ * w        [B, H] bf16           head weights
+ * k_cache  [B, Lmax, D] e4m3     indexer key cache
+ * k_scale  [B, Lmax] fp32        one scale per cached token
+ * seq_lens [B] int32, device     1 <= len_b <= Lmax (read on the device only)
+ * B >= 1; H in {16, 32, 64}; D in {64, 128}; 1 <= Lmax <= 262144; 1 <= topk <= 4096.
+ * out_idx        [B, topk] int32 ascending, -1 padded
+ * out_topk_score [B, topk] fp32 or NULL
+ */
+dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                   const float* k_scale, const int32_t* seq_lens,
+                                   int B, int Lmax, int H, int D, int topk,
+                                   int32_t* out_idx, float* out_topk_score,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * IndexCache Full/Shared schedule.  [IC] 2.1, [BA] inference-loop figure,
+ * [IS] 4.2.
+ * ------------------------------------------------------------------------ */
+
+/* Host only, no device work.  pattern: N characters from {F, S}, first one F
+ * ([IC] 2.1: the first layer is always F).  src_layer (host [N], may be NULL)
+ * receives src[l] = l for F and the nearest earlier F layer for S. */
+dsa_status indexcache_resolve(const char* pattern, int N, int32_t* src_layer);
+
+/* Called once per layer, in order, after that layer's indices are in
+ * `idx` (for an S layer: the buffer the source F layer wrote, same pointer).
+ * Work the hook enqueues on `stream` is ordered with the schedule. */
+typedef void (*indexcache_layer_fn)(int layer, int src_layer, const int32_t* idx, void* stream,
+                                    void* user);
+
+/*
+ * Runs the schedule over N layers of one prefill: an F layer runs
+ * dsa_indexer_topk_prefill with its own inputs into `tcache`; an S layer
+ * enqueues nothing and reuses `tcache` in place.
+ * q, q_scale, k, k_scale, w: host arrays of N device pointers (entries of S
+ * layers are not read and may be NULL; q_scale/k_scale arrays may be NULL).
+ * tcache [L, topk] int32, caller-owned, overwritten at every F layer.
+ * src_layer_out host [N] or NULL.  hook may be NULL.
+ * The workspace is the prefill workspace for (L, H, D, topk, dt).
+ */
+dsa_status indexcache_run_layers(const char* pattern, int N,
+                                 const void* const* q, const float* const* q_scale,
+                                 int64_t q_scale_head_stride,
+                                 const void* const* k, const float* const* k_scale,
+                                 const uint16_t* const* w,
+                                 int L, int H, int D, int topk, dsa_dtype dt,
+                                 int32_t* tcache, int32_t* src_layer_out,
+                                 indexcache_layer_fn hook, void* user,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Cross-layer overlap.  [IC] 1.2.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * idx        host array of N device pointers, each [L, topk] int32, ascending
+ *            non-negative indices then -1 padding (the selection outputs above)
+ * rows       t = row_begin, row_begin + row_stride, ... < row_end
+ *            (0 <= row_begin < row_end <= L, row_stride >= 1)
+ * out_counts [N, N] uint64, device: C[i][j] = sum over rows of |T_i(t) ∩ T_j(t)|
+ * out_ratio  [N, N] fp64, host, or NULL: C / (topk * number of rows).  When it
+ *            is given the call waits for the stream (synchronous).
+ * 1 <= N <= 64.
+ */
+dsa_status topk_overlap_matrix(const int32_t* const* idx, int N, int L, int topk,
+                               int64_t row_begin, int64_t row_end, int64_t row_stride,
+                               uint64_t* out_counts, double* out_ratio, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H */

@@ -1,0 +1,242 @@
+"""Python binding of the gfx950 lightning-indexer library (``libdsa_indexer.so``).
+
+Argument marshalling only: every function below takes torch tensors that
+already live on the GPU, passes their device pointers and the current HIP
+stream to the C entry point of the same name (declared in
+``include/dsa_indexer.h``), and raises ``DsaError`` when it returns a
+non-zero status.  Outputs and workspaces the caller does not pass are
+allocated with torch.  There is no other implementation: importing this
+package fails if the HIP library has not been built
+(``python -m sparse_attention_token_02_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime.  Import it before loading the library so the
+# library's libamdhip64.so.7 dependency resolves to that same, already-loaded
+# runtime: two HIP runtimes in one process cannot share device pointers.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_indexer.so")
+
+DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(5)
+DSA_BF16, DSA_FP8_E4M3 = 0, 1
+
+EXPORTS = (
+    "dsa_last_error", "dsa_abi_version",
+    "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill",
+    "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode",
+    "indexcache_resolve", "indexcache_run_layers", "topk_overlap_matrix",
+)
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_token_02_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+HOOK_T = ctypes.CFUNCTYPE(None, _i32, _i32, _vp, _vp, _vp)
+
+_lib.dsa_last_error.restype = ctypes.c_char_p
+_lib.dsa_last_error.argtypes = []
+_lib.dsa_abi_version.restype = _i32
+_lib.dsa_abi_version.argtypes = []
+_lib.dsa_indexer_topk_prefill_workspace.restype = _i32
+_lib.dsa_indexer_topk_prefill_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+_lib.dsa_indexer_topk_prefill.restype = _i32
+_lib.dsa_indexer_topk_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dsa_indexer_topk_decode_workspace.restype = _i32
+_lib.dsa_indexer_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+_lib.dsa_indexer_topk_decode.restype = _i32
+_lib.dsa_indexer_topk_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                         _vp, _vp, _vp, _sz, _vp]
+_lib.indexcache_resolve.restype = _i32
+_lib.indexcache_resolve.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(ctypes.c_int32)]
+_lib.indexcache_run_layers.restype = _i32
+_lib.indexcache_run_layers.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp), _i64,
+                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                       _i32, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(ctypes.c_int32),
+                                       HOOK_T, _vp, _vp, _sz, _vp]
+_lib.topk_overlap_matrix.restype = _i32
+_lib.topk_overlap_matrix.argtypes = [ctypes.POINTER(_vp), _i32, _i32, _i32, _i64, _i64, _i64, _vp,
+                                     ctypes.POINTER(ctypes.c_double), _vp]
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"dsa status {status}: {message}")
+        self.status = status
+
+
+def _check(rc: int) -> None:
+    if rc != DSA_OK:
+        raise DsaError(rc, _lib.dsa_last_error().decode())
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (for callers that want the raw C ABI)."""
+    return _lib
+
+
+def dsa_last_error() -> str:
+    return _lib.dsa_last_error().decode()
+
+
+def dsa_abi_version() -> int:
+    return _lib.dsa_abi_version()
+
+
+def _dt(dt) -> int:
+    if dt in ("fp8", DSA_FP8_E4M3):
+        return DSA_FP8_E4M3
+    if dt in ("bf16", DSA_BF16):
+        return DSA_BF16
+    raise ValueError(f"unknown dtype {dt!r}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def dsa_indexer_topk_prefill_workspace(L: int, H: int, D: int, topk: int, dt) -> int:
+    n = _sz(0)
+    _check(_lib.dsa_indexer_topk_prefill_workspace(L, H, D, topk, _dt(dt), ctypes.byref(n)))
+    return n.value
+
+
+def dsa_indexer_topk_prefill(q, q_scale, k, k_scale, w, topk: int, dt, *, q_scale_head_stride: int = 0,
+                             out_idx=None, out_topk_score=None, out_dense_score=None,
+                             want_scores: bool = False, want_dense: bool = False,
+                             workspace=None, stream=None):
+    """q [L,H,D] (uint8 e4m3 codes or bf16), k [L,D], w [L,H] bf16, scales fp32 or None.
+    Returns (idx [L,topk] int32, topk scores or None, dense scores or None)."""
+    import torch
+    L, H, D = q.shape
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((L, topk), dtype=torch.int32, device=dev)
+    if out_topk_score is None and want_scores:
+        out_topk_score = torch.empty((L, topk), dtype=torch.float32, device=dev)
+    if out_dense_score is None and want_dense:
+        out_dense_score = torch.empty((L, L), dtype=torch.float32, device=dev)
+    ws = _workspace(dsa_indexer_topk_prefill_workspace(L, H, D, topk, dt), dev, workspace)
+    _check(_lib.dsa_indexer_topk_prefill(
+        _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), L, H, D, topk, _dt(dt),
+        _ptr(out_idx), _ptr(out_topk_score), _ptr(out_dense_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_topk_score, out_dense_score
+
+
+def dsa_indexer_topk_decode_workspace(B: int, Lmax: int, H: int, D: int, topk: int) -> int:
+    n = _sz(0)
+    _check(_lib.dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk, ctypes.byref(n)))
+    return n.value
+
+
+def dsa_indexer_topk_decode(q, w, k_cache, k_scale, seq_lens, topk: int, *, out_idx=None,
+                            out_topk_score=None, want_scores: bool = False, workspace=None, stream=None):
+    """q [B,H,D] bf16, w [B,H] bf16, k_cache [B,Lmax,D] e4m3 codes, k_scale [B,Lmax] fp32,
+    seq_lens [B] int32 (device).  Returns (idx [B,topk] int32, scores or None)."""
+    import torch
+    B, H, D = q.shape
+    Lmax = k_cache.shape[1]
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    if out_topk_score is None and want_scores:
+        out_topk_score = torch.empty((B, topk), dtype=torch.float32, device=dev)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace)
+    _check(_lib.dsa_indexer_topk_decode(
+        _ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(seq_lens), B, Lmax, H, D, topk,
+        _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_topk_score
+
+
+def indexcache_resolve(pattern: str) -> list[int]:
+    N = len(pattern)
+    src = (ctypes.c_int32 * max(N, 1))()
+    _check(_lib.indexcache_resolve(pattern.encode(), N, src))
+    return list(src[:N])
+
+
+def _ptr_array(ts):
+    arr = (_vp * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = _ptr(t) if t is not None else None
+    return arr
+
+
+def indexcache_run_layers(pattern: str, q, q_scale, k, k_scale, w, topk: int, dt, *,
+                          q_scale_head_stride: int = 0, tcache=None, hook=None, workspace=None, stream=None):
+    """Per-layer lists of device tensors (entries of S layers may be None).
+    ``hook(layer, src_layer, tcache)`` runs after every layer, on the host, in
+    order (work it enqueues on the current stream is ordered with the schedule).
+    Returns (tcache, src_layer list)."""
+    import torch
+    N = len(pattern)
+    f0 = next(i for i, c in enumerate(pattern) if c == "F") if "F" in pattern else 0
+    L, H, D = q[f0].shape
+    dev = q[f0].device
+    if tcache is None:
+        tcache = torch.empty((L, topk), dtype=torch.int32, device=dev)
+    ws = _workspace(dsa_indexer_topk_prefill_workspace(L, H, D, topk, dt), dev, workspace)
+    src = (ctypes.c_int32 * max(N, 1))()
+    errors = []
+
+    def _hook(layer, src_layer, idx_ptr, stream_ptr, user):
+        try:
+            hook(layer, src_layer, tcache)
+        except Exception as e:  # surfaced after the call returns
+            errors.append(e)
+
+    cb = HOOK_T(_hook) if hook is not None else HOOK_T()
+    _check(_lib.indexcache_run_layers(
+        pattern.encode(), N, _ptr_array(q), _ptr_array(q_scale) if q_scale is not None else None,
+        q_scale_head_stride, _ptr_array(k), _ptr_array(k_scale) if k_scale is not None else None,
+        _ptr_array(w), L, H, D, topk, _dt(dt), _ptr(tcache), src, cb, None, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    if errors:
+        raise errors[0]
+    return tcache, list(src[:N])
+
+
+def topk_overlap_matrix(idx, topk: int, *, row_begin=None, row_end=None, row_stride: int = 1,
+                        out_counts=None, ratio: bool = True, stream=None):
+    """idx: list of N device int32 tensors [L, topk].  Returns (counts [N,N] uint64
+    device tensor, ratio numpy [N,N] or None).  Default rows: topk-1 .. L-1."""
+    import numpy as np
+    import torch
+    N = len(idx)
+    L = idx[0].shape[0]
+    rb = topk - 1 if row_begin is None else row_begin
+    re_ = L if row_end is None else row_end
+    if out_counts is None:
+        out_counts = torch.empty((N, N), dtype=torch.uint64, device=idx[0].device)
+    r = np.empty((N, N), dtype=np.float64) if ratio else None
+    rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if ratio else None
+    _check(_lib.topk_overlap_matrix(_ptr_array(idx), N, L, topk, rb, re_, row_stride, _ptr(out_counts), rp,
+                                    _stream(stream)))
+    return out_counts, r

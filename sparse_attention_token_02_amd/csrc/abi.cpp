@@ -1,0 +1,326 @@
+// C ABI of the lightning-indexer library: argument validation (on the host,
+// before anything touches HIP), workspace layout, the IndexCache F/S driver
+// and the overlap entry point.  See include/dsa_indexer.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dsa_indexer.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_err.clear();
+  return DSA_OK;
+}
+
+dsa_status hip_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kHeader = 256;          // work counter, kept apart from the lists
+constexpr int kMaxSlots = 256;           // persistent workgroups (one per MI355X CU)
+constexpr int kMaxTopk = 4096;
+constexpr int kMaxDenseL = 16384;
+constexpr int kMaxDecodeLmax = 262144;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int prefill_cap(int topk) {
+  const int tk = dsa::prefill_tile_keys();
+  int c = 4 * topk;
+  if (c < topk + 16 * tk) c = topk + 16 * tk;
+  return (int)align_up((size_t)c, 64);
+}
+
+int prefill_slots(int L, int H) {
+  const int rw = dsa::prefill_rows_per_item(H);
+  const int items = (L + rw - 1) / rw;
+  return items < kMaxSlots ? items : kMaxSlots;
+}
+
+size_t prefill_ws_bytes(int L, int H, int topk) {
+  const size_t per = (size_t)dsa::prefill_rows_per_item(H) * prefill_cap(topk);
+  return kHeader + 2 * align_up((size_t)prefill_slots(L, H) * per * 4, 256);
+}
+
+dsa_status check_prefill_shape(int L, int H, int D, int topk, dsa_dtype dt) {
+  if (dt != DSA_BF16 && dt != DSA_FP8_E4M3) return fail(DSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (L < 1) return fail(DSA_ERR_INVALID_ARG, "L must be >= 1 (got %d)", L);
+  if (topk < 1 || topk > kMaxTopk) return fail(DSA_ERR_INVALID_ARG, "topk must be in [1, %d] (got %d)", kMaxTopk, topk);
+  if (H < 1 || D < 1) return fail(DSA_ERR_INVALID_ARG, "H and D must be positive");
+  if (!dsa::prefill_supported((int)dt, H, D))
+    return fail(DSA_ERR_UNSUPPORTED, "prefill kernels are not built for dt=%d H=%d D=%d", (int)dt, H, D);
+  return DSA_OK;
+}
+
+int device_cus(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  *out = cus;
+  return 0;
+}
+
+struct PrefillArgs {
+  const void* q;
+  const float* q_scale;
+  int64_t qs_head_stride;
+  const void* k;
+  const float* k_scale;
+  const uint16_t* w;
+  int L, H, D, topk;
+  dsa_dtype dt;
+  int32_t* out_idx;
+  float* out_score;
+  float* out_dense;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+dsa_status validate_prefill(const PrefillArgs& a, bool check_dense = true) {
+  dsa_status st = check_prefill_shape(a.L, a.H, a.D, a.topk, a.dt);
+  if (st != DSA_OK) return st;
+  if (!a.q || !a.k || !a.w || !a.out_idx) return fail(DSA_ERR_INVALID_ARG, "q, k, w and out_idx must not be NULL");
+  if (!aligned16(a.q) || !aligned16(a.k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (a.qs_head_stride != 0 && a.qs_head_stride != 1)
+    return fail(DSA_ERR_INVALID_ARG, "q_scale_head_stride must be 0 or 1");
+  if (check_dense && a.out_dense && a.L > kMaxDenseL)
+    return fail(DSA_ERR_INVALID_ARG, "out_dense_score is only allowed for L <= %d", kMaxDenseL);
+  const size_t need = prefill_ws_bytes(a.L, a.H, a.topk);
+  if (!a.ws || a.ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, a.ws ? a.ws_bytes : (size_t)0);
+  if (!aligned16(a.ws)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return DSA_OK;
+}
+
+dsa_status launch_prefill(const PrefillArgs& a) {
+  int cus = 0;
+  if (device_cus(&cus) != 0) return fail(DSA_ERR_HIP, "no HIP device");
+  dsa::PrefillParams p{};
+  p.q = static_cast<const uint8_t*>(a.q);
+  p.q_scale = a.q_scale;
+  p.qs_row = a.qs_head_stride ? a.H : 1;
+  p.qs_head = a.qs_head_stride;
+  p.k = static_cast<const uint8_t*>(a.k);
+  p.k_scale = a.k_scale;
+  p.w = a.w;
+  p.L = a.L;
+  p.topk = a.topk;
+  p.cap = prefill_cap(a.topk);
+  p.out_idx = a.out_idx;
+  p.out_score = a.out_score;
+  p.out_dense = a.out_dense;
+  const int rw = dsa::prefill_rows_per_item(a.H);
+  p.n_items = (a.L + rw - 1) / rw;
+  const int slots = prefill_slots(a.L, a.H);
+  uint8_t* base = static_cast<uint8_t*>(a.ws);
+  p.counter = reinterpret_cast<int*>(base);
+  const size_t lst = align_up((size_t)slots * rw * p.cap * 4, 256);
+  p.ws_sc = reinterpret_cast<float*>(base + kHeader);
+  p.ws_ix = reinterpret_cast<int32_t*>(base + kHeader + lst);
+  const int grid = slots < cus ? slots : cus;
+  hipError_t e = dsa::prefill_launch(p, (int)a.dt, a.H, a.D, grid, a.stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int dsa_abi_version(void) { return 1; }
+
+dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa_dtype dt, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
+  dsa_status st = check_prefill_shape(L, H, D, topk, dt);
+  if (st != DSA_OK) return st;
+  *bytes = prefill_ws_bytes(L, H, topk);
+  return ok();
+}
+
+dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t q_scale_head_stride,
+                                    const void* k, const float* k_scale, const uint16_t* w, int L, int H,
+                                    int D, int topk, dsa_dtype dt, int32_t* out_idx, float* out_topk_score,
+                                    float* out_dense_score, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  PrefillArgs a{q, q_scale, q_scale_head_stride, k, k_scale, w, L, H, D, topk, dt, out_idx,
+                out_topk_score, out_dense_score, workspace, workspace_bytes,
+                static_cast<hipStream_t>(stream)};
+  dsa_status st = validate_prefill(a);
+  if (st != DSA_OK) return st;
+  st = launch_prefill(a);
+  if (st != DSA_OK) return st;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+
+static size_t decode_ws_bytes(int B, int Lmax) {
+  return align_up((size_t)B * Lmax * 4, 256) + (size_t)B * dsa::decode_hist_bins() * 4;
+}
+
+dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int topk, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
+  if (B < 1 || Lmax < 1 || topk < 1 || topk > kMaxTopk || H < 1 || D < 1)
+    return fail(DSA_ERR_INVALID_ARG, "bad decode sizes B=%d Lmax=%d H=%d D=%d topk=%d", B, Lmax, H, D, topk);
+  if (Lmax > kMaxDecodeLmax || !dsa::decode_supported(H, D, Lmax))
+    return fail(DSA_ERR_UNSUPPORTED, "decode kernels are not built for H=%d D=%d Lmax=%d", H, D, Lmax);
+  *bytes = decode_ws_bytes(B, Lmax);
+  return ok();
+}
+
+dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                   const float* k_scale, const int32_t* seq_lens, int B, int Lmax, int H, int D,
+                                   int topk, int32_t* out_idx, float* out_topk_score, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  dsa_status st = dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk, &need);
+  if (st != DSA_OK) return st;
+  if (!q || !w || !k_cache || !k_scale || !seq_lens || !out_idx)
+    return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache, k_scale, seq_lens and out_idx must not be NULL");
+  if (!aligned16(q) || !aligned16(k_cache)) return fail(DSA_ERR_INVALID_ARG, "q and k_cache must be 16-byte aligned");
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  dsa::DecodeParams p{};
+  p.q = q;
+  p.w = w;
+  p.cache = k_cache;
+  p.k_scale = k_scale;
+  p.lens = seq_lens;
+  p.B = B;
+  p.Lmax = Lmax;
+  p.topk = topk;
+  p.out_idx = out_idx;
+  p.out_score = out_topk_score;
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.scores = reinterpret_cast<float*>(base);
+  p.hist = reinterpret_cast<uint32_t*>(base + align_up((size_t)B * Lmax * 4, 256));
+  hipError_t e = dsa::decode_launch(p, H, D, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+
+dsa_status indexcache_resolve(const char* pattern, int N, int32_t* src_layer) {
+  if (!pattern) return fail(DSA_ERR_INVALID_ARG, "pattern must not be NULL");
+  if (N < 1) return fail(DSA_ERR_INVALID_ARG, "N must be >= 1 (got %d)", N);
+  const size_t n = strnlen(pattern, (size_t)N + 1);
+  if (n != (size_t)N) return fail(DSA_ERR_INVALID_ARG, "pattern has length %zu, expected N=%d", n, N);
+  if (pattern[0] != 'F') return fail(DSA_ERR_INVALID_ARG, "the first layer must be F (got '%c')", pattern[0]);
+  int last_f = 0;
+  for (int l = 0; l < N; ++l) {
+    const char c = pattern[l];
+    if (c != 'F' && c != 'S') return fail(DSA_ERR_INVALID_ARG, "pattern[%d] = '%c' is not F or S", l, c);
+    if (c == 'F') last_f = l;
+    if (src_layer) src_layer[l] = last_f;
+  }
+  return ok();
+}
+
+dsa_status indexcache_run_layers(const char* pattern, int N, const void* const* q, const float* const* q_scale,
+                                 int64_t q_scale_head_stride, const void* const* k,
+                                 const float* const* k_scale, const uint16_t* const* w, int L, int H, int D,
+                                 int topk, dsa_dtype dt, int32_t* tcache, int32_t* src_layer_out,
+                                 indexcache_layer_fn hook, void* user, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  std::vector<int32_t> src((size_t)(N > 0 ? N : 1));
+  dsa_status st = indexcache_resolve(pattern, N, src.data());
+  if (st != DSA_OK) return st;
+  if (!q || !k || !w) return fail(DSA_ERR_INVALID_ARG, "q, k and w pointer arrays must not be NULL");
+  if (!tcache) return fail(DSA_ERR_INVALID_ARG, "tcache must not be NULL");
+  // validate every F layer before enqueueing anything
+  for (int l = 0; l < N; ++l) {
+    if (pattern[l] != 'F') continue;
+    PrefillArgs a{q[l], q_scale ? q_scale[l] : nullptr, q_scale_head_stride, k[l], k_scale ? k_scale[l] : nullptr,
+                  w[l], L, H, D, topk, dt, tcache, nullptr, nullptr, workspace, workspace_bytes,
+                  static_cast<hipStream_t>(stream)};
+    st = validate_prefill(a, false);
+    if (st != DSA_OK) {
+      std::string m = g_err;
+      return fail(st, "layer %d: %s", l, m.c_str());
+    }
+  }
+  for (int l = 0; l < N; ++l) {
+    if (pattern[l] == 'F') {
+      PrefillArgs a{q[l], q_scale ? q_scale[l] : nullptr, q_scale_head_stride, k[l],
+                    k_scale ? k_scale[l] : nullptr, w[l], L, H, D, topk, dt, tcache, nullptr, nullptr,
+                    workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+      st = launch_prefill(a);
+      if (st != DSA_OK) {
+        std::string m = g_err;
+        return fail(st, "layer %d: %s", l, m.c_str());
+      }
+    }
+    if (hook) hook(l, src[l], tcache, stream, user);
+  }
+  if (src_layer_out) memcpy(src_layer_out, src.data(), sizeof(int32_t) * (size_t)N);
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+
+dsa_status topk_overlap_matrix(const int32_t* const* idx, int N, int L, int topk, int64_t row_begin,
+                               int64_t row_end, int64_t row_stride, uint64_t* out_counts, double* out_ratio,
+                               void* stream) {
+  if (!idx || !out_counts) return fail(DSA_ERR_INVALID_ARG, "idx and out_counts must not be NULL");
+  if (N < 1 || N > dsa::OVERLAP_MAX_N) return fail(DSA_ERR_INVALID_ARG, "N must be in [1, %d]", dsa::OVERLAP_MAX_N);
+  if (L < 1 || topk < 1) return fail(DSA_ERR_INVALID_ARG, "L and topk must be >= 1");
+  if (row_begin < 0 || row_end > L || row_begin >= row_end || row_stride < 1)
+    return fail(DSA_ERR_INVALID_ARG, "rows must satisfy 0 <= row_begin < row_end <= L and row_stride >= 1");
+  for (int i = 0; i < N; ++i)
+    if (!idx[i]) return fail(DSA_ERR_INVALID_ARG, "idx[%d] is NULL", i);
+  dsa::OverlapParams p{};
+  for (int i = 0; i < N; ++i) p.idx[i] = idx[i];
+  p.N = N;
+  p.L = L;
+  p.topk = topk;
+  p.row_begin = row_begin;
+  p.row_end = row_end;
+  p.row_stride = row_stride;
+  p.counts = reinterpret_cast<unsigned long long*>(out_counts);
+  int cus = 0;
+  if (device_cus(&cus) != 0) return fail(DSA_ERR_HIP, "no HIP device");
+  const long long nrows = (row_end - row_begin + row_stride - 1) / row_stride;
+  long long grid = 4LL * cus;
+  if (grid > nrows) grid = nrows;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::overlap_launch(p, (int)grid, s);
+  if (e != hipSuccess) return hip_fail(e, "overlap launch");
+  if (out_ratio) {
+    std::vector<uint64_t> h((size_t)N * N);
+    e = hipMemcpyAsync(h.data(), out_counts, h.size() * sizeof(uint64_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "overlap readback");
+    const double den = (double)topk * (double)nrows;
+    for (size_t i = 0; i < h.size(); ++i) out_ratio[i] = (double)h[i] / den;
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa_indexer.h"
+
+namespace dsa {
+
+constexpr int OVERLAP_MAX_N = 64;
+
+struct PrefillParams {
+  const uint8_t* q;          // [L, H, D] e4m3 codes or bf16 (as bytes)
+  const float* q_scale;      // nullable; element (t, h) at t*qs_row + h*qs_head
+  int64_t qs_row;
+  int64_t qs_head;
+  const uint8_t* k;          // [L, D]
+  const float* k_scale;      // [L], nullable
+  const uint16_t* w;         // [L, H] bf16
+  int L;
+  int topk;
+  int cap;                   // candidate list capacity per row
+  int32_t* out_idx;          // [L, topk]
+  float* out_score;          // [L, topk], nullable
+  float* out_dense;          // [L, L], nullable
+  float* ws_sc;              // [grid, rows_per_item, cap]
+  int32_t* ws_ix;            // [grid, rows_per_item, cap]
+  int* counter;              // work counter
+  int n_items;               // ceil(L / rows_per_item)
+};
+
+struct DecodeParams {
+  const uint16_t* q;         // [B, H, D] bf16
+  const uint16_t* w;         // [B, H] bf16
+  const uint8_t* cache;      // [B, Lmax, D] e4m3
+  const float* k_scale;      // [B, Lmax]
+  const int32_t* lens;       // [B] device
+  int B;
+  int Lmax;
+  int topk;
+  int32_t* out_idx;          // [B, topk]
+  float* out_score;          // [B, topk], nullable
+  float* scores;             // workspace [B, Lmax]
+  uint32_t* hist;            // workspace [B, 4096]
+};
+
+struct OverlapParams {
+  const int32_t* idx[OVERLAP_MAX_N];   // N device pointers, each [L, topk]
+  int N;
+  int L;
+  int topk;
+  long long row_begin;
+  long long row_end;
+  long long row_stride;
+  unsigned long long* counts;          // [N, N] device
+};
+
+// prefill.hip
+bool prefill_supported(int dt, int H, int D);
+int prefill_rows_per_item(int H);
+int prefill_tile_keys();
+hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream);
+
+// decode.hip
+bool decode_supported(int H, int D, int Lmax);
+size_t decode_select_lds_bytes(int Lmax);
+int decode_hist_bins();
+hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream);
+
+// overlap.hip
+size_t overlap_lds_bytes(int N);
+hipError_t overlap_launch(const OverlapParams& p, int grid, hipStream_t stream);
+
+}  // namespace dsa

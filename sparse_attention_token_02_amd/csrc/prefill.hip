@@ -1,0 +1,376 @@
+// Fused prefill lightning indexer + streaming top-k for gfx950.
+//
+// What is computed (IndexCache deep-dive report, abstract and section 1.1:
+// a multi-head ReLU-gated dot product, run in FP8, that scores every earlier
+// token and keeps the k best):
+//   score(t, s) = k_scale[s] * sum_h w[t,h] * q_scale[t,h] * ReLU(q[t,h] . k[s]),  s <= t
+// and, per query row t, the min(k, t+1) best keys under "score descending,
+// key index ascending", written in ascending key order and padded with -1.
+//
+// Design (one work item = RW consecutive query rows, 8 waves):
+// * Score contraction on MFMA.  Index heads sit on the MFMA row dimension, so
+//   the head sum stays inside a lane: with the 32x32 accumulator layout a lane
+//   owns one key column and 16 rows, and the rows are assigned so that all 16
+//   belong to one query (H >= 16) or to two queries of 8 heads (H == 8).  The
+//   two lane halves therefore hold two different queries: no cross-lane
+//   reduction at all.  Keys are the MFMA column dimension.
+//   fp8 path: v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit block
+//   scales); bf16 path: v_mfma_f32_32x32x16_bf16.  Products are exact, the
+//   accumulation is fp32.
+// * Keys are staged through LDS in tiles of 64, double buffered; every wave
+//   reuses each tile for its own queries.  Query operands and the folded head
+//   weights w*q_scale stay in registers for the whole work item.
+// * Epilogue per (query, key): sum_h w_eff * max(x, 0), times k_scale, causal
+//   mask.  The L x L score matrix is never stored (the optional dense output
+//   exists for small debugging runs only).
+// * Streaming top-k: each row keeps a threshold tau (the current k-th best
+//   score) and appends keys with score > tau, in ascending key order, to a
+//   candidate list in the per-workgroup workspace.  Keys arrive in ascending
+//   index order, so a later key that ties the k-th score always loses the tie
+//   and "strictly greater" is the exact filter.  When a list could overflow
+//   during the next tile, the whole workgroup compacts it to exactly k
+//   entries (block_select), which also raises tau.  At the end of the work
+//   item the same routine selects the final k and writes them out in order.
+// * Persistent grid: one workgroup per CU pulls work items from an atomic
+//   counter, longest (highest t) first, which balances the causal triangle.
+#include "device_common.hpp"
+#include "block_select.hpp"
+#include "kernels.hpp"
+
+namespace dsa {
+
+namespace {
+
+constexpr int NT = 512;      // threads per workgroup (8 waves)
+constexpr int WAVES = NT / 64;
+constexpr int TK = 64;       // keys per LDS tile
+
+template <int DT, int H, int D>
+struct PfCfg {
+  static constexpr bool FP8 = (DT == DSA_FP8_E4M3);
+  static constexpr int HB = H < 16 ? H : 16;        // heads of one query in one lane-block
+  static constexpr int QPH = 16 / HB;               // queries per lane half
+  static constexpr int QPW = 2 * QPH;               // queries per wave
+  static constexpr int MB = H < 16 ? 1 : H / 16;    // 32-row MFMA blocks per wave
+  static constexpr int ESZ = FP8 ? 1 : 2;           // bytes per element
+  static constexpr int KM = FP8 ? 64 : 16;          // K of one MFMA
+  static constexpr int KS = D / KM;                 // MFMAs along D
+  static constexpr int SB = FP8 ? 32 : 16;          // bytes per lane per MFMA operand
+  static constexpr int ROWB = D * ESZ;              // bytes of one key / one query head
+  static constexpr int RW = WAVES * QPW;            // query rows per work item
+  static constexpr int STRIDE = ROWB + 16;          // padded LDS row (bank-conflict free b128 reads)
+  static constexpr int CHUNKS = TK * ROWB / 16;     // 16-byte pieces of a key tile
+  static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  static_assert(H == 8 || (H % 16 == 0 && H <= 64), "unsupported head count");
+  static_assert(D % KM == 0 && ROWB / 2 == KS * SB, "unsupported head dim");
+  static_assert(RW <= 32, "row mask is 32 bits");
+};
+
+template <bool FP8> struct Opnd;
+template <> struct Opnd<true> { typedef v8i T; };
+template <> struct Opnd<false> { typedef v8bf T; };
+
+template <bool FP8>
+__device__ __forceinline__ typename Opnd<FP8>::T load_opnd(const uint8_t* p) {
+  if constexpr (FP8) {
+    v4i a = *reinterpret_cast<const v4i*>(p);
+    v4i b = *reinterpret_cast<const v4i*>(p + 16);
+    return v8i{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  } else {
+    v4i a = *reinterpret_cast<const v4i*>(p);
+    return __builtin_bit_cast(v8bf, a);
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ typename Opnd<FP8>::T zero_opnd() {
+  if constexpr (FP8) {
+    return v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  } else {
+    return __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ v16f mma(typename Opnd<FP8>::T a, typename Opnd<FP8>::T b, v16f c) {
+  if constexpr (FP8) return mfma_fp8(a, b, c);
+  else return mfma_bf16(a, b, c);
+}
+
+}  // namespace
+
+template <int DT, int H, int D>
+__global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
+  using C = PfCfg<DT, H, D>;
+  using OT = typename Opnd<C::FP8>::T;
+
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][TK * C::STRIDE];
+  __shared__ float kscale_sh[2][TK];
+  __shared__ SelectShared<NT> ssh;
+  __shared__ int row_cnt[C::RW];
+  __shared__ float row_tau[C::RW];
+  __shared__ uint32_t need_mask;
+  __shared__ int item_sh;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int kh = lane >> 5;      // lane half: K half of the operands, query half of the result
+  const int col = lane & 31;     // MFMA row (A operand) / column (B operand, result)
+
+  const size_t slot_elems = (size_t)C::RW * p.cap;
+  float* wsc = p.ws_sc + (size_t)blockIdx.x * slot_elems;
+  int* wix = p.ws_ix + (size_t)blockIdx.x * slot_elems;
+  const int L = p.L;
+
+  // A-operand row `col` of block mb holds (query slot, head) of the result row
+  // with the same index: result row m has lane half (m>>2)&1 and register
+  // j = 4*(m>>3) + (m&3).
+  const int a_hf = (col >> 2) & 1;
+  const int a_j = ((col >> 3) << 2) | (col & 3);
+  const int a_slot = a_hf * C::QPH + a_j / C::HB;
+  const int a_head_lo = a_j % C::HB;
+
+  if (tid == 0) need_mask = 0u;
+
+  for (;;) {
+    if (tid == 0) item_sh = atomicAdd(p.counter, 1);
+    __syncthreads();
+    const int item = item_sh;
+    if (item >= p.n_items) break;
+    const int t0 = (p.n_items - 1 - item) * C::RW;
+    const int kend = min(t0 + C::RW, L);
+    const int ntiles = (kend + TK - 1) / TK;
+
+    // ---- query operands and folded head weights (registers for the whole item)
+    OT qa[C::MB][C::KS];
+    {
+      const int t = t0 + wave * C::QPW + a_slot;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const int head = 16 * mb + a_head_lo;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          if (t < L) {
+            const uint8_t* src = p.q + ((size_t)t * H + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
+            qa[mb][ks] = load_opnd<C::FP8>(src);
+          } else {
+            qa[mb][ks] = zero_opnd<C::FP8>();
+          }
+        }
+      }
+    }
+    float wr[C::MB][16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int t = t0 + wave * C::QPW + kh * C::QPH + j / C::HB;
+#pragma unroll
+      for (int mb = 0; mb < C::MB; ++mb) {
+        const int head = 16 * mb + j % C::HB;
+        float v = 0.f;
+        if (t < L) {
+          v = bf16_to_f32(p.w[(size_t)t * H + head]);
+          if (p.q_scale) v *= p.q_scale[(size_t)t * p.qs_row + (size_t)head * p.qs_head];
+        }
+        wr[mb][j] = v;
+      }
+    }
+    int cnt[C::QPH];
+    float tau[C::QPH];
+#pragma unroll
+    for (int r = 0; r < C::QPH; ++r) {
+      cnt[r] = 0;
+      tau[r] = -__builtin_inff();
+    }
+    const int row_base = wave * C::QPW + kh * C::QPH;   // local row of slot r is row_base + r
+
+    // ---- key tile staging
+    v4i gbuf[C::CPT];
+    float gks = 1.f;
+    auto gload = [&](int kt) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int ci = tid + c * NT;
+        gbuf[c] = v4i{0, 0, 0, 0};
+        if (ci < C::CHUNKS) {
+          const int key = kt + ci / (C::ROWB / 16);
+          if (key < L)
+            gbuf[c] = *reinterpret_cast<const v4i*>(p.k + (size_t)key * C::ROWB + (ci % (C::ROWB / 16)) * 16);
+        }
+      }
+      if (tid < TK) gks = (p.k_scale && kt + tid < L) ? p.k_scale[kt + tid] : 1.f;
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int c = 0; c < C::CPT; ++c) {
+        const int ci = tid + c * NT;
+        if (ci < C::CHUNKS) {
+          const int kl = ci / (C::ROWB / 16);
+          *reinterpret_cast<v4i*>(&ktile[buf][kl * C::STRIDE + (ci % (C::ROWB / 16)) * 16]) = gbuf[c];
+        }
+      }
+      if (tid < TK) kscale_sh[buf][tid] = gks;
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int kt = it * TK;
+      const int buf = it & 1;
+      if (it + 1 < ntiles) gload(kt + TK);
+
+#pragma unroll
+      for (int sub = 0; sub < TK / 32; ++sub) {
+        const int s0 = kt + 32 * sub;
+        if (s0 < kend) {
+          const uint8_t* bp = &ktile[buf][(32 * sub + col) * C::STRIDE + kh * (C::ROWB / 2)];
+          v16f acc[C::MB];
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) acc[mb] = v16f{};
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks) {
+            const OT b = load_opnd<C::FP8>(bp + ks * C::SB);
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) acc[mb] = mma<C::FP8>(qa[mb][ks], b, acc[mb]);
+          }
+          // head-weighted ReLU sum, in-lane
+          float part[C::QPH][4];
+#pragma unroll
+          for (int r = 0; r < C::QPH; ++r)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) part[r][u] = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              part[j / C::HB][j & 3] = fmaf(wr[mb][j], fmaxf(acc[mb][j], 0.f), part[j / C::HB][j & 3]);
+          const float ksc = kscale_sh[buf][32 * sub + col];
+          const int s = s0 + col;
+#pragma unroll
+          for (int r = 0; r < C::QPH; ++r) {
+            const float score = ((part[r][0] + part[r][1]) + (part[r][2] + part[r][3])) * ksc;
+            const int tr = t0 + row_base + r;
+            const bool valid = (s <= tr) && (tr < L);
+            if (p.out_dense && tr < L && s < L)
+              p.out_dense[(size_t)tr * L + s] = valid ? score : -__builtin_inff();
+            const bool pass = valid && score > tau[r];
+            const uint64_t m = ballot64(pass);
+            const uint32_t mh = kh ? (uint32_t)(m >> 32) : (uint32_t)m;
+            if (pass) {
+              const int pos = cnt[r] + __popc(mh & ((1u << col) - 1u));
+              const size_t o = (size_t)(row_base + r) * p.cap + pos;
+              wsc[o] = score;
+              wix[o] = s;
+            }
+            cnt[r] += __popc(mh);
+          }
+        }
+      }
+
+      // room for one more tile in every list, else ask for a compaction
+#pragma unroll
+      for (int r = 0; r < C::QPH; ++r) {
+        if (col == 0 && cnt[r] + TK > p.cap) {
+          row_cnt[row_base + r] = cnt[r];
+          atomicOr(&need_mask, 1u << (row_base + r));
+        }
+      }
+      if (it + 1 < ntiles) lstore(buf ^ 1);
+      __syncthreads();
+      const uint32_t mask = need_mask;
+      if (mask) {
+        for (int rl = 0; rl < C::RW; ++rl) {
+          if ((mask >> rl) & 1u) {
+            float* rs = wsc + (size_t)rl * p.cap;
+            int* ri = wix + (size_t)rl * p.cap;
+            const int n = block_select<NT>(rs, ri, row_cnt[rl], p.topk, rs, ri, 0, ssh, &row_tau[rl]);
+            if (tid == 0) row_cnt[rl] = n;
+            __syncthreads();
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < C::QPH; ++r) {
+          if ((mask >> (row_base + r)) & 1u) {
+            cnt[r] = row_cnt[row_base + r];
+            tau[r] = row_tau[row_base + r];
+          }
+        }
+        __syncthreads();
+        if (tid == 0) need_mask = 0u;
+        __syncthreads();
+      }
+    }
+
+    // ---- final selection, written to the output rows in ascending key order
+#pragma unroll
+    for (int r = 0; r < C::QPH; ++r)
+      if (col == 0) row_cnt[row_base + r] = cnt[r];
+    __syncthreads();
+    for (int rl = 0; rl < C::RW; ++rl) {
+      const int t = t0 + rl;
+      if (t >= L) break;
+      int* dix = p.out_idx + (size_t)t * p.topk;
+      float* dsc = p.out_score ? p.out_score + (size_t)t * p.topk : nullptr;
+      block_select<NT>(wsc + (size_t)rl * p.cap, wix + (size_t)rl * p.cap, row_cnt[rl], p.topk, dsc, dix,
+                       p.topk, ssh, nullptr);
+    }
+  }
+}
+
+__global__ void prefill_prepare_kernel(int* counter, float* dense, long long n_dense) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *counter = 0;
+  if (dense) {
+    for (long long j = i; j < n_dense; j += (long long)gridDim.x * blockDim.x) dense[j] = -__builtin_inff();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+template <int DT, int H, int D>
+static void launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((prefill_kernel<DT, H, D>), dim3(grid), dim3(NT), 0, stream, p);
+}
+
+int prefill_rows_per_item(int H) { return WAVES * 2 * (H < 16 ? 16 / H : 1); }
+
+bool prefill_supported(int dt, int H, int D) {
+  const bool fp8 = dt == DSA_FP8_E4M3;
+  if (!(H == 8 || H == 16 || H == 32 || H == 64)) return false;
+  if (D != 64 && D != 128) return false;
+  if (!fp8 && H == 64 && D == 128) return false;   // register budget
+  return true;
+}
+
+int prefill_tile_keys() { return TK; }
+
+hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream) {
+  const long long n_dense = p.out_dense ? (long long)p.L * p.L : 0;
+  const int pg = n_dense ? 1024 : 1;
+  hipLaunchKernelGGL(prefill_prepare_kernel, dim3(pg), dim3(256), 0, stream, p.counter, p.out_dense, n_dense);
+#define DSA_PF_CASE(DT_, H_, D_) \
+  if (dt == DT_ && H == H_ && D == D_) { launch_one<DT_, H_, D_>(p, grid, stream); return hipGetLastError(); }
+  DSA_PF_CASE(DSA_FP8_E4M3, 64, 128)
+  DSA_PF_CASE(DSA_FP8_E4M3, 64, 64)
+  DSA_PF_CASE(DSA_FP8_E4M3, 32, 128)
+  DSA_PF_CASE(DSA_FP8_E4M3, 32, 64)
+  DSA_PF_CASE(DSA_FP8_E4M3, 16, 128)
+  DSA_PF_CASE(DSA_FP8_E4M3, 16, 64)
+  DSA_PF_CASE(DSA_FP8_E4M3, 8, 128)
+  DSA_PF_CASE(DSA_FP8_E4M3, 8, 64)
+  DSA_PF_CASE(DSA_BF16, 64, 64)
+  DSA_PF_CASE(DSA_BF16, 32, 128)
+  DSA_PF_CASE(DSA_BF16, 32, 64)
+  DSA_PF_CASE(DSA_BF16, 16, 128)
+  DSA_PF_CASE(DSA_BF16, 16, 64)
+  DSA_PF_CASE(DSA_BF16, 8, 128)
+  DSA_PF_CASE(DSA_BF16, 8, 64)
+#undef DSA_PF_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

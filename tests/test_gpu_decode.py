@@ -1,0 +1,102 @@
+"""GPU parity of the decode indexer scan + top-k against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+from tests import parity
+from tests.gpu_util import dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_02_amd as m
+    return m
+
+
+def _small_inputs(B, Lmax, H, D, lens, seed=0):
+    rng = np.random.default_rng(seed)
+    cache, ks = gen.quant_rows_e4m3(rng.standard_normal((B * Lmax, D)).astype(np.float32))
+    q = gen.bf16_bits(rng.standard_normal((B, H, D)).astype(np.float32))
+    w = gen.bf16_bits((rng.standard_normal((B, H)) / 8).astype(np.float32))
+    return {"cache": cache.reshape(B, Lmax, D), "k_scale": ks.reshape(B, Lmax), "q": q, "w": w,
+            "lens": np.asarray(lens, dtype=np.int32)}
+
+
+def _run(dsa, inp, topk):
+    import torch
+    out = dsa.dsa_indexer_topk_decode(dev(inp["q"]), dev(inp["w"]), dev(inp["cache"]), dev(inp["k_scale"]),
+                                      dev(inp["lens"]), topk, want_scores=True)
+    torch.cuda.synchronize()
+    return host(out[0]), host(out[1])
+
+
+def _compare(idx, sc, inp, topk, seqs=None):
+    seqs = range(len(inp["lens"])) if seqs is None else seqs
+    res = oracle.decode(inp["q"], inp["w"], inp["cache"], inp["k_scale"], inp["lens"], topk, return_scores=True)
+    for b in seqs:
+        err = parity.check_row(idx[b], res["o"][b], res["A"][b], topk, g_score=sc[b])
+        assert err is None, (b, err)
+
+
+@pytest.mark.parametrize("H,D", [(64, 128), (32, 64), (16, 128)])
+def test_decode_small_every_sequence(dsa, H, D):
+    lens = [5000, 4097, 256, 100, 1, 2049]
+    inp = _small_inputs(6, 5000, H, D, lens, seed=H + D)
+    note(f"decode small H={H} D={D}")
+    idx, sc = _run(dsa, inp, 256)
+    _compare(idx, sc, inp, 256)
+
+
+def test_decode_one_giant_tie_takes_lowest_indices(dsa):
+    """q = 0: every score is 0, the threshold bin holds every key (more than fit
+    in the candidate buffer), and the selection must be keys 0..k-1."""
+    Lmax, topk = 20000, 300
+    inp = _small_inputs(2, Lmax, 64, 128, [Lmax, 7000], seed=5)
+    inp["q"][:] = 0
+    note("decode all-zero tie")
+    idx, sc = _run(dsa, inp, topk)
+    for b in range(2):
+        assert idx[b].tolist() == list(range(topk))
+        assert np.all(sc[b] == 0)
+
+
+def test_decode_deterministic(dsa):
+    inp = _small_inputs(3, 9000, 64, 128, [9000, 8000, 3000], seed=9)
+    note("decode determinism")
+    a = _run(dsa, inp, 512)
+    b = _run(dsa, inp, 512)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.int32), b[1].view(np.int32))
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_decode_128k_full_size_sampled_sequences(dsa, ragged):
+    """B=32 sequences of a 131072-token fp8 cache, at full size in the launch
+    configuration the benchmark times; oracle on a seeded sample of sequences."""
+    import torch
+    from synth.gpu import DeviceGen
+    cfg = gen.ragged_decode_config() if ragged else gen.CONFIGS["decode_128k"]
+    note(f"decode 128k ragged={ragged} generate")
+    d = DeviceGen().decode_inputs(cfg)
+    note(f"decode 128k ragged={ragged} kernel")
+    idx, sc = dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], cfg["topk"],
+                                          want_scores=True)
+    torch.cuda.synchronize()
+    idx, sc = host(idx), host(sc)
+    seqs = [0, 13, 31]
+    hi = gen.decode_inputs(cfg, seqs=seqs)
+    assert np.array_equal(host(d["cache"][seqs[1]]), hi["cache"][1])
+    assert np.array_equal(host(d["k_scale"][seqs[2]]), hi["k_scale"][2])
+    res = oracle.decode(hi["q"], hi["w"], hi["cache"], hi["k_scale"], hi["lens"], cfg["topk"], return_scores=True)
+    for i, b in enumerate(seqs):
+        err = parity.check_row(idx[b], res["o"][i], res["A"][i], cfg["topk"], g_score=sc[b])
+        assert err is None, (b, err)
+    lens = gen.decode_lens(cfg)
+    for b in range(cfg["B"]):
+        v = idx[b][idx[b] >= 0]
+        assert len(v) == min(cfg["topk"], lens[b]) and np.all(np.diff(v) > 0) and v[-1] < lens[b]
