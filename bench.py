@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the lightning-indexer hot path on one MI355X.
+
+One step = one fused prefill indexer + top-k over a single L=32768 sequence
+(H=64 index heads, D=128, k=2048, fp8 e4m3 q/k with per-token scales, bf16
+head weights, 1% planted heavy keys) followed by one decode indexer + top-k
+over a batch of 32 sequences with 131072-token fp8 key caches.  Inputs are
+seeded synthetic data generated on the device before timing; the timed region
+holds only the two library calls.
+
+Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
+TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
+in algorithmic GB/s is reported beside it.  Other workloads
+(``--workload tiny|prefill_196k|fs_47``) print their own line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer prefill TFLOP/s (%fp8 MFMA peak) + decode HBM GB/s at 128K ctx"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(L, H, D):
+    return 2.0 * H * D * L * (L + 1) / 2.0
+
+
+def decode_bytes(lens, H, D, topk, B):
+    # cache bytes + per-token scales + queries + weights + output indices
+    return float(sum(int(n) for n in lens) * (D + 4) + B * H * D * 2 + B * H * 2 + B * topk * 4)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_attention_token_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, per_launch_units):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline_prefill(cfg, budget_s=12.0):
+    """The fp64 oracle on a seeded sample of query rows of the same workload."""
+    import numpy as np
+    import oracle
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    L, H, D, topk = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
+    rng = np.random.default_rng(7)
+    keys = gen.prefill_inputs(cfg, rows=[0])
+    pairs = 0
+    nrows = 0
+    el = 0.0
+    while el < budget_s and nrows < 4096:
+        rows = np.sort(rng.choice(L, size=16, replace=False))
+        inp = gen.prefill_inputs(cfg, rows=rows, with_keys=False)
+        ts = time.perf_counter()
+        oracle.prefill(inp["q"], inp["q_scale"], keys["k"], keys["k_scale"], inp["w"], "fp8", topk, rows=rows)
+        el += time.perf_counter() - ts
+        pairs += int(np.sum(rows + 1))
+        nrows += len(rows)
+    tflops = pairs * 2.0 * H * D / el / 1e12
+    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nrows} seeded query rows of the L={L} prefill ({pairs} causal pairs, fp64 oracle, "
+                      f"{el:.1f} s of oracle time)",
+            "rows_per_s": round(nrows / el, 3),
+            "full_workload_s_extrapolated": round(L * (L + 1) / 2 / (pairs / el), 1)}
+
+
+def run_main(args):
+    import torch
+    import sparse_attention_token_02_amd as dsa
+    from synth import gen
+    from synth.gpu import DeviceGen
+
+    dev = torch.device("cuda:0")
+    g = DeviceGen(dev)
+    pcfg = gen.CONFIGS["prefill_32k"]
+    dcfg = gen.CONFIGS["decode_128k"]
+    L, H, D, topk = pcfg["L"], pcfg["H"], pcfg["D"], pcfg["topk"]
+    log("generating prefill inputs")
+    p = g.prefill_inputs(pcfg)
+    out_idx = torch.empty((L, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_indexer_topk_prefill_workspace(L, H, D, topk, "fp8"), dtype=torch.uint8, device=dev)
+    log("generating decode inputs (two cache copies, each larger than the 256 MB MALL)")
+    dd = [g.decode_inputs(dcfg)]
+    dd.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in dd[0].items()})
+    B, Lmax = dcfg["B"], dcfg["Lmax"]
+    d_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    dws = torch.empty(dsa.dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def prefill():
+        dsa.dsa_indexer_topk_prefill(p["q"], p["q_scale"], p["k"], p["k_scale"], p["w"], topk, "fp8",
+                                     out_idx=out_idx, workspace=ws, stream=stream)
+
+    turn = [0]
+
+    def decode():
+        d = dd[turn[0] & 1]
+        turn[0] += 1
+        dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk,
+                                    out_idx=d_idx, workspace=dws, stream=stream)
+
+    log("warmup + timed steps")
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+    ev = []
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        prefill()
+        e[1].record(stream)
+        decode()
+        e[2].record(stream)
+        ev.append(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    pf_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    dc_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
+    med = lambda xs: xs[len(xs) // 2]
+    pf_avg = sum(pf_ms) / len(pf_ms)
+    dc_avg = sum(dc_ms) / len(dc_ms)
+    flops = prefill_flops(L, H, D)
+    lens = gen.decode_lens(dcfg)
+    dbytes = decode_bytes(lens, H, D, topk, B)
+    pf_tflops = flops / (pf_avg * 1e-3) / 1e12
+    dc_gbps = dbytes / (dc_avg * 1e-3) / 1e9
+    ms_per_step = wall * 1e3 / args.steps
+    res = {
+        "metric": METRIC,
+        "value": round(pf_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate); decode bf16 x e4m3->bf16",
+        "data": "synthetic (seeded, generated on device)",
+        "config": {"workload": "prefill L=32768 H=64 D=128 k=2048 fp8 + decode B=32 x 131072 fp8 cache k=2048",
+                   "prefill_L": L, "heads": H, "head_dim": D, "topk": topk, "decode_batch": B,
+                   "decode_ctx": Lmax},
+        "prefill_ms": round(pf_avg, 4), "prefill_ms_median": round(med(pf_ms), 4),
+        "prefill_rows_per_s": round(L / (pf_avg * 1e-3), 1),
+        "decode_us": round(dc_avg * 1e3, 2), "decode_us_median": round(med(dc_ms) * 1e3, 2),
+        "decode_GBps": round(dc_gbps, 1),
+        "decode_rows_per_s": round(B / (dc_avg * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": load_traffic("prefill_32k", 1)},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dc_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": round(dc_gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic("decode_128k", 1)},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a row sample)")
+        res["cpu_baseline"] = cpu_baseline_prefill(pcfg, budget_s=args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def run_workload(args):
+    import torch
+    import sparse_attention_token_02_amd as dsa
+    from synth import gen
+    from synth.gpu import DeviceGen
+    dev = torch.device("cuda:0")
+    g = DeviceGen(dev)
+    stream = torch.cuda.current_stream(dev)
+    name = args.workload
+    if name in ("tiny", "prefill_196k", "prefill_32k"):
+        cfg = gen.CONFIGS[name]
+        L, H, D, topk = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
+        p = g.prefill_inputs(cfg)
+        out = torch.empty((L, topk), dtype=torch.int32, device=dev)
+        ws = torch.empty(dsa.dsa_indexer_topk_prefill_workspace(L, H, D, topk, cfg["dtype"]), dtype=torch.uint8,
+                         device=dev)
+        fn = lambda: dsa.dsa_indexer_topk_prefill(p["q"], p["q_scale"], p["k"], p["k_scale"], p["w"], topk,
+                                                  cfg["dtype"], out_idx=out, workspace=ws, stream=stream)
+        ms = time_calls(fn, args.steps, args.warmup, stream)
+        avg = sum(ms) / len(ms)
+        tf = prefill_flops(L, H, D) / (avg * 1e-3) / 1e12
+        peak = PEAK_FP8_TFLOPS if cfg["dtype"] == "fp8" else PEAK_BF16_TFLOPS
+        return {"metric": METRIC, "workload": name, "value": round(tf, 2), "unit": "TFLOP/s",
+                "ms_per_call": round(avg, 4), "rows_per_s": round(L / (avg * 1e-3), 1),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                             "frac": round(tf / peak, 4), "traffic": None},
+                "config": {"workload": name, **{k: v for k, v in cfg.items() if k != "kind"}}}
+    if name == "fs_47":
+        return run_fs(args, g, dsa, gen, stream)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def run_fs(args, g, dsa, gen, stream):
+    """Layer-reuse schedule over 47 layers: indexer time for each pattern and
+    the 47x47 overlap of the all-F run."""
+    import torch
+    cfg = gen.CONFIGS["fs_47"]
+    L, H, D, topk, N = cfg["L"], cfg["H"], cfg["D"], cfg["topk"], cfg["N"]
+    dev = g.device
+    log("generating 47 layers")
+    layers = [g.fs_layer_inputs(cfg, l) for l in range(N)]
+    ws = torch.empty(dsa.dsa_indexer_topk_prefill_workspace(L, H, D, topk, "fp8"), dtype=torch.uint8, device=dev)
+    tcache = torch.empty((L, topk), dtype=torch.int32, device=dev)
+    args_l = lambda key: [layers[l][key] for l in range(N)]
+    res = {"metric": METRIC, "workload": "fs_47", "config": {"workload": "fs_47", "N": N, "L": L, "H": H, "D": D,
+                                                              "topk": topk}}
+    times = {}
+    for pname, pat in gen.FS_PATTERNS.items():
+        fn = lambda: dsa.indexcache_run_layers(pat, args_l("q"), args_l("q_scale"), args_l("k"), args_l("k_scale"),
+                                               args_l("w"), topk, "fp8", tcache=tcache, workspace=ws, stream=stream)
+        ms = time_calls(fn, max(1, args.steps), max(0, args.warmup), stream)
+        times[pname] = sum(ms) / len(ms)
+    nF = {p: pat.count("F") for p, pat in gen.FS_PATTERNS.items()}
+    res["indexer_ms"] = {p: round(v, 3) for p, v in times.items()}
+    res["indexer_time_saved_frac"] = {p: round(1 - times[p] / times["all_F"], 4) for p in times}
+    res["ideal_saved_frac"] = {p: round(1 - nF[p] / N, 4) for p in times}
+    tf = nF["all_F"] * prefill_flops(L, H, D) / (times["all_F"] * 1e-3) / 1e12
+    res["value"] = round(tf, 2)
+    res["unit"] = "TFLOP/s"
+    # overlap of the all-F run: keep every layer's indices
+    keep = [torch.empty((L, topk), dtype=torch.int32, device=dev) for _ in range(N)]
+    hook = lambda layer, src, tc: keep[layer].copy_(tc)
+    dsa.indexcache_run_layers(gen.FS_PATTERNS["all_F"], args_l("q"), args_l("q_scale"), args_l("k"),
+                              args_l("k_scale"), args_l("w"), topk, "fp8", tcache=tcache, hook=hook, workspace=ws,
+                              stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    counts, ratio = dsa.topk_overlap_matrix(keep, topk)
+    torch.cuda.synchronize()
+    res["overlap_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+    res["overlap_adjacent_mean"] = round(float(sum(ratio[i, i + 1] for i in range(N - 1)) / (N - 1)), 4)
+    res["overlap_matrix"] = [[round(float(x), 4) for x in row] for row in ratio]
+    for pname, pat in gen.FS_PATTERNS.items():
+        src = dsa.indexcache_resolve(pat)
+        s_layers = [l for l in range(N) if pat[l] == "S"]
+        if s_layers:
+            res.setdefault("s_layer_mean_overlap_with_source", {})[pname] = round(
+                float(sum(ratio[l, src[l]] for l in s_layers) / len(s_layers)), 4)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="main")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--reference-copy-mb", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB three times (a plain copy of known "
+                         "size, used to calibrate memory-traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"this benchmark runs on one GPU only (asked for --gpus {args.gpus}); the indexer path is measured "
+              "per GPU and is not sharded across GPUs", file=sys.stderr)
+        sys.exit(2)
+    res = run_main(args) if args.workload == "main" else run_workload(args)
+    if args.reference_copy_mb > 0:
+        import torch
+        n = args.reference_copy_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["reference_copy_bytes"] = n
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -45,12 +45,7 @@ constexpr int kMaxDecodeLmax = 262144;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int prefill_cap(int topk) {
-  const int tk = dsa::prefill_tile_keys();
-  int c = 4 * topk;
-  if (c < topk + 16 * tk) c = topk + 16 * tk;
-  return (int)align_up((size_t)c, 64);
-}
+int prefill_cap(int dt, int H, int D, int topk) { return dsa::prefill_list_capacity(dt, H, D, topk); }
 
 int prefill_slots(int L, int H) {
   const int rw = dsa::prefill_rows_per_item(H);
@@ -58,8 +53,8 @@ int prefill_slots(int L, int H) {
   return items < kMaxSlots ? items : kMaxSlots;
 }
 
-size_t prefill_ws_bytes(int L, int H, int topk) {
-  const size_t per = (size_t)dsa::prefill_rows_per_item(H) * prefill_cap(topk);
+size_t prefill_ws_bytes(int L, int H, int D, int topk, dsa_dtype dt) {
+  const size_t per = (size_t)dsa::prefill_rows_per_item(H) * prefill_cap((int)dt, H, D, topk);
   return kHeader + 2 * align_up((size_t)prefill_slots(L, H) * per * 4, 256);
 }
 
@@ -70,6 +65,8 @@ dsa_status check_prefill_shape(int L, int H, int D, int topk, dsa_dtype dt) {
   if (H < 1 || D < 1) return fail(DSA_ERR_INVALID_ARG, "H and D must be positive");
   if (!dsa::prefill_supported((int)dt, H, D))
     return fail(DSA_ERR_UNSUPPORTED, "prefill kernels are not built for dt=%d H=%d D=%d", (int)dt, H, D);
+  if (prefill_cap((int)dt, H, D, topk) == 0)
+    return fail(DSA_ERR_UNSUPPORTED, "topk=%d does not fit the candidate lists in LDS for H=%d D=%d", topk, H, D);
   return DSA_OK;
 }
 
@@ -108,7 +105,7 @@ dsa_status validate_prefill(const PrefillArgs& a, bool check_dense = true) {
     return fail(DSA_ERR_INVALID_ARG, "q_scale_head_stride must be 0 or 1");
   if (check_dense && a.out_dense && a.L > kMaxDenseL)
     return fail(DSA_ERR_INVALID_ARG, "out_dense_score is only allowed for L <= %d", kMaxDenseL);
-  const size_t need = prefill_ws_bytes(a.L, a.H, a.topk);
+  const size_t need = prefill_ws_bytes(a.L, a.H, a.D, a.topk, a.dt);
   if (!a.ws || a.ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, a.ws ? a.ws_bytes : (size_t)0);
   if (!aligned16(a.ws)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
@@ -128,7 +125,7 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   p.w = a.w;
   p.L = a.L;
   p.topk = a.topk;
-  p.cap = prefill_cap(a.topk);
+  p.cap = prefill_cap((int)a.dt, a.H, a.D, a.topk);
   p.out_idx = a.out_idx;
   p.out_score = a.out_score;
   p.out_dense = a.out_dense;
@@ -158,7 +155,7 @@ dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
   dsa_status st = check_prefill_shape(L, H, D, topk, dt);
   if (st != DSA_OK) return st;
-  *bytes = prefill_ws_bytes(L, H, topk);
+  *bytes = prefill_ws_bytes(L, H, D, topk, dt);
   return ok();
 }
 
@@ -179,9 +176,34 @@ dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t
 
 // ---------------------------------------------------------------------------
 
-static size_t decode_ws_bytes(int B, int Lmax) {
-  return align_up((size_t)B * Lmax * 4, 256) + (size_t)B * dsa::decode_hist_bins() * 4;
+// Decode workspace: score rows [B, ld] fp32, histograms [B, 4096], counters
+// [B, 2], selected lists [B, topk], candidate keys and indices [B, Lmax] each.
+struct DecodeWs {
+  size_t scores, hist, counts, sel, ckey, cidx, total;
+  int ld;
+};
+
+static DecodeWs decode_ws(int B, int Lmax, int topk) {
+  DecodeWs w{};
+  w.ld = (int)align_up((size_t)Lmax, 64);
+  size_t off = 0;
+  w.scores = off;
+  off += align_up((size_t)B * w.ld * 4, 256);
+  w.hist = off;
+  off += align_up((size_t)B * dsa::decode_hist_bins() * 4, 256);
+  w.counts = off;
+  off += align_up((size_t)B * 2 * 4, 256);
+  w.sel = off;
+  off += align_up((size_t)B * topk * 4, 256);
+  w.ckey = off;
+  off += align_up((size_t)B * Lmax * 4, 256);
+  w.cidx = off;
+  off += align_up((size_t)B * Lmax * 4, 256);
+  w.total = off;
+  return w;
 }
+
+static size_t decode_ws_bytes(int B, int Lmax, int topk) { return decode_ws(B, Lmax, topk).total; }
 
 dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int topk, size_t* bytes) {
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
@@ -189,7 +211,7 @@ dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int 
     return fail(DSA_ERR_INVALID_ARG, "bad decode sizes B=%d Lmax=%d H=%d D=%d topk=%d", B, Lmax, H, D, topk);
   if (Lmax > kMaxDecodeLmax || !dsa::decode_supported(H, D, Lmax))
     return fail(DSA_ERR_UNSUPPORTED, "decode kernels are not built for H=%d D=%d Lmax=%d", H, D, Lmax);
-  *bytes = decode_ws_bytes(B, Lmax);
+  *bytes = decode_ws_bytes(B, Lmax, topk);
   return ok();
 }
 
@@ -218,8 +240,14 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
   p.out_idx = out_idx;
   p.out_score = out_topk_score;
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  p.scores = reinterpret_cast<float*>(base);
-  p.hist = reinterpret_cast<uint32_t*>(base + align_up((size_t)B * Lmax * 4, 256));
+  const DecodeWs lay = decode_ws(B, Lmax, topk);
+  p.ld = lay.ld;
+  p.scores = reinterpret_cast<float*>(base + lay.scores);
+  p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
+  p.counts = reinterpret_cast<int*>(base + lay.counts);
+  p.sel_idx = reinterpret_cast<int*>(base + lay.sel);
+  p.cand_key = reinterpret_cast<uint32_t*>(base + lay.ckey);
+  p.cand_idx = reinterpret_cast<int*>(base + lay.cidx);
   hipError_t e = dsa::decode_launch(p, H, D, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();

@@ -41,8 +41,13 @@ struct DecodeParams {
   int topk;
   int32_t* out_idx;          // [B, topk]
   float* out_score;          // [B, topk], nullable
-  float* scores;             // workspace [B, Lmax]
+  int ld;                    // row stride of the score rows (Lmax rounded up to 64)
+  float* scores;             // workspace [B, ld]
   uint32_t* hist;            // workspace [B, 4096]
+  int* counts;               // workspace [B, 2]: selected, candidates
+  int* sel_idx;              // workspace [B, topk]
+  uint32_t* cand_key;        // workspace [B, Lmax]
+  int* cand_idx;             // workspace [B, Lmax]
 };
 
 struct OverlapParams {
@@ -60,11 +65,12 @@ struct OverlapParams {
 bool prefill_supported(int dt, int H, int D);
 int prefill_rows_per_item(int H);
 int prefill_tile_keys();
+int prefill_list_capacity(int dt, int H, int D, int topk);
 hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream);
 
 // decode.hip
 bool decode_supported(int H, int D, int Lmax);
-size_t decode_select_lds_bytes(int Lmax);
+size_t decode_finalize_lds_bytes(int Lmax);
 int decode_hist_bins();
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream);
 

@@ -43,7 +43,7 @@ namespace {
 
 constexpr int NT = 512;      // threads per workgroup (8 waves)
 constexpr int WAVES = NT / 64;
-constexpr int TK = 64;       // keys per LDS tile
+constexpr int TK = 128;      // keys per LDS tile
 
 template <int DT, int H, int D>
 struct PfCfg {
@@ -64,6 +64,20 @@ struct PfCfg {
   static_assert(H == 8 || (H % 16 == 0 && H <= 64), "unsupported head count");
   static_assert(D % KM == 0 && ROWB / 2 == KS * SB, "unsupported head dim");
   static_assert(RW <= 32, "row mask is 32 bits");
+};
+
+template <int DT, int H, int D>
+struct PfShared {
+  using C = PfCfg<DT, H, D>;
+  uint8_t ktile[2][TK * C::STRIDE];     // double-buffered key tile
+  float kscale[2][TK];
+  float stage_sc[C::RW][TK];            // this tile's accepted candidates, per row
+  int stage_ix[C::RW][TK];
+  SelectShared<NT> sel;
+  int row_cnt[C::RW];
+  float row_tau[C::RW];
+  uint32_t need_mask;
+  int item;
 };
 
 template <bool FP8> struct Opnd;
@@ -103,14 +117,10 @@ template <int DT, int H, int D>
 __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
   using C = PfCfg<DT, H, D>;
   using OT = typename Opnd<C::FP8>::T;
-
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][TK * C::STRIDE];
-  __shared__ float kscale_sh[2][TK];
-  __shared__ SelectShared<NT> ssh;
-  __shared__ int row_cnt[C::RW];
-  __shared__ float row_tau[C::RW];
-  __shared__ uint32_t need_mask;
-  __shared__ int item_sh;
+  __shared__ PfShared<DT, H, D> sh;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];   // list staging for the select
+  float* lsc = reinterpret_cast<float*>(dyn_lds);
+  int* lix = reinterpret_cast<int*>(dyn_lds + (size_t)p.cap * sizeof(float));
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -131,12 +141,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
   const int a_slot = a_hf * C::QPH + a_j / C::HB;
   const int a_head_lo = a_j % C::HB;
 
-  if (tid == 0) need_mask = 0u;
+  if (tid == 0) sh.need_mask = 0u;
 
   for (;;) {
-    if (tid == 0) item_sh = atomicAdd(p.counter, 1);
+    if (tid == 0) sh.item = atomicAdd(p.counter, 1);
     __syncthreads();
-    const int item = item_sh;
+    const int item = sh.item;
     if (item >= p.n_items) break;
     const int t0 = (p.n_items - 1 - item) * C::RW;
     const int kend = min(t0 + C::RW, L);
@@ -175,11 +185,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         wr[mb][j] = v;
       }
     }
-    int cnt[C::QPH];
-    float tau[C::QPH];
+    int cnt[C::QPH];      // list length of each of this lane's rows (uniform in the lane half)
+    int scnt[C::QPH];     // entries staged in LDS during the current tile
+    float tau[C::QPH];    // current k-th best score (-inf until the first compaction)
 #pragma unroll
     for (int r = 0; r < C::QPH; ++r) {
       cnt[r] = 0;
+      scnt[r] = 0;
       tau[r] = -__builtin_inff();
     }
     const int row_base = wave * C::QPW + kh * C::QPH;   // local row of slot r is row_base + r
@@ -187,18 +199,17 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     // ---- key tile staging
     v4i gbuf[C::CPT];
     float gks = 1.f;
+    // Key tile loads are unconditional: keys past the end read the last key
+    // (such keys are always masked), so no branch merges into gbuf and no
+    // early wait is forced on the prefetch.
     auto gload = [&](int kt) {
 #pragma unroll
       for (int c = 0; c < C::CPT; ++c) {
-        const int ci = tid + c * NT;
-        gbuf[c] = v4i{0, 0, 0, 0};
-        if (ci < C::CHUNKS) {
-          const int key = kt + ci / (C::ROWB / 16);
-          if (key < L)
-            gbuf[c] = *reinterpret_cast<const v4i*>(p.k + (size_t)key * C::ROWB + (ci % (C::ROWB / 16)) * 16);
-        }
+        const int ci = min(tid + c * NT, C::CHUNKS - 1);
+        const int key = min(kt + ci / (C::ROWB / 16), L - 1);
+        gbuf[c] = *reinterpret_cast<const v4i*>(p.k + (size_t)key * C::ROWB + (ci % (C::ROWB / 16)) * 16);
       }
-      if (tid < TK) gks = (p.k_scale && kt + tid < L) ? p.k_scale[kt + tid] : 1.f;
+      gks = p.k_scale ? p.k_scale[min(kt + (tid & (TK - 1)), L - 1)] : 1.f;
     };
     auto lstore = [&](int buf) {
 #pragma unroll
@@ -206,10 +217,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int ci = tid + c * NT;
         if (ci < C::CHUNKS) {
           const int kl = ci / (C::ROWB / 16);
-          *reinterpret_cast<v4i*>(&ktile[buf][kl * C::STRIDE + (ci % (C::ROWB / 16)) * 16]) = gbuf[c];
+          *reinterpret_cast<v4i*>(&sh.ktile[buf][kl * C::STRIDE + (ci % (C::ROWB / 16)) * 16]) = gbuf[c];
         }
       }
-      if (tid < TK) kscale_sh[buf][tid] = gks;
+      if (tid < TK) sh.kscale[buf][tid] = gks;
     };
 
     gload(0);
@@ -225,7 +236,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       for (int sub = 0; sub < TK / 32; ++sub) {
         const int s0 = kt + 32 * sub;
         if (s0 < kend) {
-          const uint8_t* bp = &ktile[buf][(32 * sub + col) * C::STRIDE + kh * (C::ROWB / 2)];
+          const uint8_t* bp = &sh.ktile[buf][(32 * sub + col) * C::STRIDE + kh * (C::ROWB / 2)];
           v16f acc[C::MB];
 #pragma unroll
           for (int mb = 0; mb < C::MB; ++mb) acc[mb] = v16f{};
@@ -246,7 +257,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int j = 0; j < 16; ++j)
               part[j / C::HB][j & 3] = fmaf(wr[mb][j], fmaxf(acc[mb][j], 0.f), part[j / C::HB][j & 3]);
-          const float ksc = kscale_sh[buf][32 * sub + col];
+          const float ksc = sh.kscale[buf][32 * sub + col];
           const int s = s0 + col;
 #pragma unroll
           for (int r = 0; r < C::QPH; ++r) {
@@ -259,46 +270,60 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
             const uint64_t m = ballot64(pass);
             const uint32_t mh = kh ? (uint32_t)(m >> 32) : (uint32_t)m;
             if (pass) {
-              const int pos = cnt[r] + __popc(mh & ((1u << col) - 1u));
-              const size_t o = (size_t)(row_base + r) * p.cap + pos;
-              wsc[o] = score;
-              wix[o] = s;
+              const int pos = scnt[r] + __popc(mh & ((1u << col) - 1u));
+              sh.stage_sc[row_base + r][pos] = score;
+              sh.stage_ix[row_base + r][pos] = s;
             }
-            cnt[r] += __popc(mh);
+            scnt[r] += __popc(mh);
           }
         }
       }
 
-      // room for one more tile in every list, else ask for a compaction
+      // ---- move this tile's staged candidates to the rows' lists (one burst per row)
+#pragma unroll
+      for (int rr = 0; rr < C::QPW; ++rr) {
+        const int hf = rr / C::QPH, r = rr % C::QPH;
+        const int n = __builtin_amdgcn_readlane(scnt[r], hf * 32);
+        const int c0 = __builtin_amdgcn_readlane(cnt[r], hf * 32);
+        const int row = wave * C::QPW + rr;
+        for (int e = lane; e < n; e += 64) {
+          wsc[(size_t)row * p.cap + c0 + e] = sh.stage_sc[row][e];
+          wix[(size_t)row * p.cap + c0 + e] = sh.stage_ix[row][e];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < C::QPH; ++r) {
+        cnt[r] += scnt[r];
+        scnt[r] = 0;
+        // room for one more tile in every list, else ask for a compaction
         if (col == 0 && cnt[r] + TK > p.cap) {
-          row_cnt[row_base + r] = cnt[r];
-          atomicOr(&need_mask, 1u << (row_base + r));
+          sh.row_cnt[row_base + r] = cnt[r];
+          atomicOr(&sh.need_mask, 1u << (row_base + r));
         }
       }
       if (it + 1 < ntiles) lstore(buf ^ 1);
       __syncthreads();
-      const uint32_t mask = need_mask;
+      const uint32_t mask = sh.need_mask;
       if (mask) {
         for (int rl = 0; rl < C::RW; ++rl) {
           if ((mask >> rl) & 1u) {
             float* rs = wsc + (size_t)rl * p.cap;
             int* ri = wix + (size_t)rl * p.cap;
-            const int n = block_select<NT>(rs, ri, row_cnt[rl], p.topk, rs, ri, 0, ssh, &row_tau[rl]);
-            if (tid == 0) row_cnt[rl] = n;
+            const int n = block_select<NT>(rs, ri, sh.row_cnt[rl], p.topk, rs, ri, 0, sh.sel, lsc, lix,
+                                           &sh.row_tau[rl]);
+            if (tid == 0) sh.row_cnt[rl] = n;
             __syncthreads();
           }
         }
 #pragma unroll
         for (int r = 0; r < C::QPH; ++r) {
           if ((mask >> (row_base + r)) & 1u) {
-            cnt[r] = row_cnt[row_base + r];
-            tau[r] = row_tau[row_base + r];
+            cnt[r] = sh.row_cnt[row_base + r];
+            tau[r] = sh.row_tau[row_base + r];
           }
         }
         __syncthreads();
-        if (tid == 0) need_mask = 0u;
+        if (tid == 0) sh.need_mask = 0u;
         __syncthreads();
       }
     }
@@ -306,15 +331,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     // ---- final selection, written to the output rows in ascending key order
 #pragma unroll
     for (int r = 0; r < C::QPH; ++r)
-      if (col == 0) row_cnt[row_base + r] = cnt[r];
+      if (col == 0) sh.row_cnt[row_base + r] = cnt[r];
     __syncthreads();
     for (int rl = 0; rl < C::RW; ++rl) {
       const int t = t0 + rl;
       if (t >= L) break;
       int* dix = p.out_idx + (size_t)t * p.topk;
       float* dsc = p.out_score ? p.out_score + (size_t)t * p.topk : nullptr;
-      block_select<NT>(wsc + (size_t)rl * p.cap, wix + (size_t)rl * p.cap, row_cnt[rl], p.topk, dsc, dix,
-                       p.topk, ssh, nullptr);
+      block_select<NT>(wsc + (size_t)rl * p.cap, wix + (size_t)rl * p.cap, sh.row_cnt[rl], p.topk, dsc, dix,
+                       p.topk, sh.sel, lsc, lix, nullptr);
     }
   }
 }
@@ -332,8 +357,18 @@ __global__ void prefill_prepare_kernel(int* counter, float* dense, long long n_d
 // ---------------------------------------------------------------------------
 
 template <int DT, int H, int D>
-static void launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<DT, H, D>), dim3(grid), dim3(NT), 0, stream, p);
+static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
+  const size_t dyn = (size_t)p.cap * 8;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DT, H, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((prefill_kernel<DT, H, D>), dim3(grid), dim3(NT), dyn, stream, p);
+  return hipGetLastError();
+}
+
+template <int DT, int H, int D>
+static size_t static_lds() {
+  return sizeof(PfShared<DT, H, D>);
 }
 
 int prefill_rows_per_item(int H) { return WAVES * 2 * (H < 16 ? 16 / H : 1); }
@@ -348,12 +383,47 @@ bool prefill_supported(int dt, int H, int D) {
 
 int prefill_tile_keys() { return TK; }
 
+// Candidate list capacity per row: 4*topk when the LDS allows (the select
+// stages one list in LDS next to the kernel's static shared memory), never
+// less than topk plus one tile.  Returns 0 if no capacity fits.
+int prefill_list_capacity(int dt, int H, int D, int topk) {
+  size_t st = 0;
+#define DSA_PF_LDS(DT_, H_, D_) \
+  if (dt == DT_ && H == H_ && D == D_) st = static_lds<DT_, H_, D_>();
+  DSA_PF_LDS(DSA_FP8_E4M3, 64, 128)
+  DSA_PF_LDS(DSA_FP8_E4M3, 64, 64)
+  DSA_PF_LDS(DSA_FP8_E4M3, 32, 128)
+  DSA_PF_LDS(DSA_FP8_E4M3, 32, 64)
+  DSA_PF_LDS(DSA_FP8_E4M3, 16, 128)
+  DSA_PF_LDS(DSA_FP8_E4M3, 16, 64)
+  DSA_PF_LDS(DSA_FP8_E4M3, 8, 128)
+  DSA_PF_LDS(DSA_FP8_E4M3, 8, 64)
+  DSA_PF_LDS(DSA_BF16, 64, 64)
+  DSA_PF_LDS(DSA_BF16, 32, 128)
+  DSA_PF_LDS(DSA_BF16, 32, 64)
+  DSA_PF_LDS(DSA_BF16, 16, 128)
+  DSA_PF_LDS(DSA_BF16, 16, 64)
+  DSA_PF_LDS(DSA_BF16, 8, 128)
+  DSA_PF_LDS(DSA_BF16, 8, 64)
+#undef DSA_PF_LDS
+  if (st == 0) return 0;
+  const size_t lds_limit = 160 * 1024;
+  if (st + 8 * (size_t)(topk + TK) > lds_limit) return 0;
+  size_t cap = 4 * (size_t)topk;
+  if (cap < (size_t)topk + 16 * TK) cap = (size_t)topk + 16 * TK;
+  const size_t max_cap = (lds_limit - st) / 8 / 64 * 64;
+  if (cap > max_cap) cap = max_cap;
+  cap = cap / 64 * 64;
+  if (cap < (size_t)topk + TK) return 0;
+  return (int)cap;
+}
+
 hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream) {
   const long long n_dense = p.out_dense ? (long long)p.L * p.L : 0;
   const int pg = n_dense ? 1024 : 1;
   hipLaunchKernelGGL(prefill_prepare_kernel, dim3(pg), dim3(256), 0, stream, p.counter, p.out_dense, n_dense);
 #define DSA_PF_CASE(DT_, H_, D_) \
-  if (dt == DT_ && H == H_ && D == D_) { launch_one<DT_, H_, D_>(p, grid, stream); return hipGetLastError(); }
+  if (dt == DT_ && H == H_ && D == D_) return launch_one<DT_, H_, D_>(p, grid, stream);
   DSA_PF_CASE(DSA_FP8_E4M3, 64, 128)
   DSA_PF_CASE(DSA_FP8_E4M3, 64, 64)
   DSA_PF_CASE(DSA_FP8_E4M3, 32, 128)

@@ -53,6 +53,14 @@ def test_decode_small_every_sequence(dsa, H, D):
     _compare(idx, sc, inp, 256)
 
 
+def test_decode_odd_cache_length(dsa):
+    lens = [3001, 2999, 1500, 2049]
+    inp = _small_inputs(4, 3001, 64, 128, lens, seed=11)
+    note("decode odd Lmax=3001")
+    idx, sc = _run(dsa, inp, 2048)
+    _compare(idx, sc, inp, 2048)
+
+
 def test_decode_one_giant_tie_takes_lowest_indices(dsa):
     """q = 0: every score is 0, the threshold bin holds every key (more than fit
     in the candidate buffer), and the selection must be keys 0..k-1."""
