@@ -24,6 +24,8 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # inputs are finite by contract: max(x, 0) needs no NaN-quieting instruction
+          "-fno-honor-nans",
           "-Wno-unused-command-line-argument",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

@@ -21,6 +21,7 @@ struct PrefillParams {
   int L;
   int topk;
   int cap;                   // candidate list capacity per row
+  int sample_m;              // keys per row in the threshold sample (0: no sample)
   int32_t* out_idx;          // [L, topk]
   float* out_score;          // [L, topk], nullable
   float* out_dense;          // [L, L], nullable
@@ -66,6 +67,7 @@ bool prefill_supported(int dt, int H, int D);
 int prefill_rows_per_item(int H);
 int prefill_tile_keys();
 int prefill_list_capacity(int dt, int H, int D, int topk);
+int prefill_sample_keys(int H, int cap);
 hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream);
 
 // decode.hip
