@@ -126,7 +126,7 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   p.L = a.L;
   p.topk = a.topk;
   p.cap = prefill_cap((int)a.dt, a.H, a.D, a.topk);
-  p.sample_m = dsa::prefill_sample_keys(a.H, p.cap);
+  p.sample_m = dsa::prefill_sample_keys((int)a.dt, a.H, a.D);
   p.out_idx = a.out_idx;
   p.out_score = a.out_score;
   p.out_dense = a.out_dense;

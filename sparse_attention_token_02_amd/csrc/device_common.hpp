@@ -49,4 +49,15 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Orders LDS accesses between the lanes of one wave: everything before it
+// (including other lanes' stores and atomics) is visible to every lane after
+// it.  The hardware already executes a wave's LDS instructions in order; the
+// fences stop the compiler from treating a lane's own earlier store as the
+// value of a later load (other lanes may have written the location since).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace dsa

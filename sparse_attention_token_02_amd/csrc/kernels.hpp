@@ -65,9 +65,8 @@ struct OverlapParams {
 // prefill.hip
 bool prefill_supported(int dt, int H, int D);
 int prefill_rows_per_item(int H);
-int prefill_tile_keys();
 int prefill_list_capacity(int dt, int H, int D, int topk);
-int prefill_sample_keys(int H, int cap);
+int prefill_sample_keys(int dt, int H, int D);
 hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream);
 
 // decode.hip

@@ -8,33 +8,42 @@
 // key index ascending", written in ascending key order and padded with -1.
 //
 // Design (one work item = RW consecutive query rows, 8 waves):
-// * Score contraction on MFMA.  Index heads sit on the MFMA row dimension, so
-//   the head sum stays inside a lane: with the 32x32 accumulator layout a lane
-//   owns one key column and 16 rows, and the rows are assigned so that all 16
-//   belong to one query (H >= 16) or to two queries of 8 heads (H == 8).  The
-//   two lane halves therefore hold two different queries: no cross-lane
-//   reduction at all.  Keys are the MFMA column dimension.
+// * Score contraction on MFMA.  Index heads sit on the MFMA row dimension and
+//   keys on the column dimension.  With the 32x32 accumulator layout a lane
+//   owns one key column and 16 rows of each 32-row block.
+//   H >= 32: a wave serves one query; block i holds heads 32i..32i+31, so the
+//   two lane halves hold different heads of the same query.  After the
+//   in-lane head sums the halves trade one partial sum per pair of 32-key
+//   subtiles, which leaves every lane with the full score of a distinct key.
+//   H <= 16: the rows of the single block belong to one query per lane half
+//   (two queries of 8 heads for H == 8): no cross-lane step at all.
 //   fp8 path: v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit block
 //   scales); bf16 path: v_mfma_f32_32x32x16_bf16.  Products are exact, the
 //   accumulation is fp32.
-// * Keys are staged through LDS in tiles of 64, double buffered; every wave
+// * Keys are staged through LDS in tiles of 128, double buffered; every wave
 //   reuses each tile for its own queries.  Query operands and the folded head
-//   weights w*q_scale stay in registers for the whole work item.
+//   weights w*q_scale stay in registers for the whole work item.  Inside a
+//   tile the MFMAs of one head block overlap the VALU epilogue of the
+//   previous one (two accumulators, explicit issue groups).
 // * Epilogue per (query, key): sum_h w_eff * max(x, 0), times k_scale, causal
 //   mask.  The L x L score matrix is never stored (the optional dense output
 //   exists for small debugging runs only).
-// * Streaming top-k: each row keeps a threshold tau (the current k-th best
-//   score) and appends keys with score > tau, in ascending key order, to a
-//   candidate list in the per-workgroup workspace.  Keys arrive in ascending
-//   index order, so a later key that ties the k-th score always loses the tie
-//   and "strictly greater" is the exact filter.  When a list could overflow
-//   during the next tile, the whole workgroup compacts it to exactly k
-//   entries (block_select), which also raises tau.  At the end of the work
-//   item the same routine selects the final k and writes them out in order.
+// * Streaming top-k: each row keeps a threshold (the larger of the current
+//   k-th best score tau and a sample estimate tau0) and appends keys strictly
+//   above it, in ascending key order, to a candidate list in the
+//   per-workgroup workspace.  Keys arrive in ascending index order, so a
+//   later key that ties the k-th score always loses the tie and "strictly
+//   greater" is exact for tau.  tau0 comes from scoring a strided sample of
+//   keys first; a row whose list ends shorter than min(k, t+1) may have lost
+//   keys to it, and its item is recomputed without the sample.  When a list
+//   could overflow during the next tile, the wave that owns it compacts it to
+//   exactly k entries (a wave-level radix select), which also raises tau.  At
+//   the end of the work item the same routine selects the final k of each
+//   row and writes them out in order.
 // * Persistent grid: one workgroup per CU pulls work items from an atomic
 //   counter, longest (highest t) first, which balances the causal triangle.
 #include "device_common.hpp"
-#include "block_select.hpp"
+#include "wave_select.hpp"
 #include "kernels.hpp"
 
 namespace dsa {
@@ -43,104 +52,50 @@ namespace {
 
 constexpr int NT = 512;      // threads per workgroup (8 waves)
 constexpr int WAVES = NT / 64;
-constexpr int TK = 128;      // keys per LDS tile
 
 template <int DT, int H, int D>
 struct PfCfg {
   static constexpr bool FP8 = (DT == DSA_FP8_E4M3);
-  static constexpr int HB = H < 16 ? H : 16;        // heads of one query in one lane-block
-  static constexpr int QPH = 16 / HB;               // queries per lane half
-  static constexpr int QPW = 2 * QPH;               // queries per wave
-  static constexpr int MB = H < 16 ? 1 : H / 16;    // 32-row MFMA blocks per wave
+  // H >= 32: one query per wave; each 32-row MFMA block holds 32 of its heads,
+  // so the two lane halves hold different heads of the same query and one
+  // cross-half add finishes the head sum.  H <= 16: each lane half holds its
+  // own queries (16/H of them) and the head sum stays inside a lane.
+  static constexpr bool SPLIT = H >= 32;
+  static constexpr int HB = H < 16 ? H : 16;        // heads of one query in one lane-block (H <= 16)
+  static constexpr int QPH = SPLIT ? 1 : 16 / HB;   // query slots per lane
+  static constexpr int QPW = SPLIT ? 1 : 2 * QPH;   // queries per wave
+  static constexpr int MB = SPLIT ? H / 32 : 1;     // 32-row MFMA blocks per wave
   static constexpr int ESZ = FP8 ? 1 : 2;           // bytes per element
   static constexpr int KM = FP8 ? 64 : 16;          // K of one MFMA
   static constexpr int KS = D / KM;                 // MFMAs along D
   static constexpr int SB = FP8 ? 32 : 16;          // bytes per lane per MFMA operand
   static constexpr int ROWB = D * ESZ;              // bytes of one key / one query head
+  // keys per LDS tile: 256 for one query per wave and key rows of at most
+  // 128 bytes (halves the per-tile barriers), else 128 (LDS budget)
+  static constexpr int TK = (ROWB <= 128 && SPLIT) ? 256 : 128;
   static constexpr int RW = WAVES * QPW;            // query rows per work item
   static constexpr int STRIDE = ROWB + 16;          // padded LDS row (bank-conflict free b128 reads)
   static constexpr int CHUNKS = TK * ROWB / 16;     // 16-byte pieces of a key tile
   static constexpr int CPT = (CHUNKS + NT - 1) / NT;
-  static_assert(H == 8 || (H % 16 == 0 && H <= 64), "unsupported head count");
+  static_assert(H == 8 || H == 16 || H == 32 || H == 64, "unsupported head count");
   static_assert(D % KM == 0 && ROWB / 2 == KS * SB, "unsupported head dim");
   static_assert(RW <= 32, "row mask is 32 bits");
+  // query slot of accumulator register j (result row 8(j/4) + 4*half + j%4)
+  static __device__ __forceinline__ int slot_of(int j) { return SPLIT ? 0 : j / HB; }
 };
 
 template <int DT, int H, int D>
 struct PfShared {
   using C = PfCfg<DT, H, D>;
-  uint8_t ktile[2][TK * C::STRIDE];     // double-buffered key tile
-  float kscale[2][TK];
-  float stage_sc[C::RW][TK];            // this tile's accepted candidates, per row
-  int stage_ix[C::RW][TK];
-  SelectShared<NT> sel;
-  uint32_t whist[WAVES][256];           // per-wave histogram for the sample quantile
+  uint8_t ktile[2][C::TK * C::STRIDE];     // double-buffered key tile
+  __attribute__((aligned(16))) float kscale[2][C::TK];
+  float stage_sc[C::RW][C::TK];            // this tile's accepted candidates, per row
+  int stage_ix[C::RW][C::TK];
+  uint32_t whist[WAVES][256];              // per-wave radix histogram (selection, sample quantile)
+  __attribute__((aligned(16))) float weff[C::RW * H];   // folded head weights w*q_scale of the item's rows
   int row_cnt[C::RW];
-  float row_tau[C::RW];
-  uint32_t need_mask;
   int item;
 };
-
-// k-th largest order-preserving key (kp >= 1) among the n floats vals[0..n),
-// computed by one wave: MSB radix select below the bits all entries share.
-__device__ uint32_t wave_kth_key(const float* vals, int n, int kp, uint32_t* hist) {
-  const int lane = __lane_id();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = lane; i < n; i += 64) {
-    const uint32_t k = ordered_key(vals[i]);
-    lo = min(lo, k);
-    hi = max(hi, k);
-  }
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (lo == hi) return lo;
-  const int top = 31 - __clz(lo ^ hi);
-  uint32_t pmask = (top == 31) ? 0u : (0xFFFFFFFFu << (top + 1));
-  uint32_t prefix = hi & pmask;
-  int need = kp;
-  for (int bit = top; bit >= 0;) {
-    const int nb = bit + 1 < 8 ? bit + 1 : 8;
-    const int shift = bit + 1 - nb;
-    const uint32_t dm = (1u << nb) - 1u;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
-    for (int i = lane; i < n; i += 64) {
-      const uint32_t k = ordered_key(vals[i]);
-      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dm], 1u);
-    }
-    uint32_t h[4], sum = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      h[b] = hist[4 * lane + b];
-      sum += h[b];
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = (uint32_t)__shfl_down((int)incl, o);
-      if (lane + o < 64) incl += t;
-    }
-    uint32_t cum = incl - sum;
-    int dig = -1, above = 0;
-#pragma unroll
-    for (int b = 3; b >= 0; --b) {
-      if (cum < (uint32_t)need && cum + h[b] >= (uint32_t)need) {
-        dig = 4 * lane + b;
-        above = (int)cum;
-      }
-      cum += h[b];
-    }
-    const uint64_t who = ballot64(dig >= 0);
-    const int src = __ffsll((long long)who) - 1;
-    dig = __builtin_amdgcn_readlane(dig, src);
-    above = __builtin_amdgcn_readlane(above, src);
-    need -= above;
-    prefix |= (uint32_t)dig << shift;
-    pmask |= dm << shift;
-    bit -= nb;
-  }
-  return prefix;
-}
 
 template <bool FP8> struct Opnd;
 template <> struct Opnd<true> { typedef v8i T; };
@@ -180,11 +135,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
   using C = PfCfg<DT, H, D>;
   using OT = typename Opnd<C::FP8>::T;
   __shared__ PfShared<DT, H, D> sh;
-  // dynamic LDS: the list being selected (scores, then indices), or during the
-  // sample phase the sampled scores of every row (RW rows x sample_m floats)
+  // dynamic LDS: the sampled scores of every row (RW rows x sample_m floats)
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-  float* lsc = reinterpret_cast<float*>(dyn_lds);
-  int* lix = reinterpret_cast<int*>(dyn_lds + (size_t)p.cap * sizeof(float));
   float* smp = reinterpret_cast<float*>(dyn_lds);
 
   const int tid = threadIdx.x;
@@ -198,15 +150,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
   int* wix = p.ws_ix + (size_t)blockIdx.x * slot_elems;
   const int L = p.L;
 
-  // A-operand row `col` of block mb holds (query slot, head) of the result row
-  // with the same index: result row m has lane half (m>>2)&1 and register
+  // A-operand row `col` of block mb holds the (query slot, head) of the result
+  // row with the same index: result row m has lane half (m>>2)&1 and register
   // j = 4*(m>>3) + (m&3).
   const int a_hf = (col >> 2) & 1;
   const int a_j = ((col >> 3) << 2) | (col & 3);
-  const int a_slot = a_hf * C::QPH + a_j / C::HB;
-  const int a_head_lo = a_j % C::HB;
-
-  if (tid == 0) sh.need_mask = 0u;
+  const int a_slot = C::SPLIT ? 0 : a_hf * C::QPH + a_j / C::HB;
+  const int a_head = C::SPLIT ? col : a_j % C::HB;   // head within block mb (block stride 32 or 16)
+  constexpr int HSTRIDE = C::SPLIT ? 32 : 16;
 
   for (;;) {
     if (tid == 0) sh.item = atomicAdd(p.counter, 1);
@@ -215,7 +166,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     if (item >= p.n_items) break;
     const int t0 = (p.n_items - 1 - item) * C::RW;
     const int kend = min(t0 + C::RW, L);
-    const int ntiles = (kend + TK - 1) / TK;
+    const int ntiles = (kend + C::TK - 1) / C::TK;
 
     // ---- query operands and folded head weights (registers for the whole item)
     OT qa[C::MB][C::KS];
@@ -223,7 +174,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       const int t = t0 + wave * C::QPW + a_slot;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        const int head = 16 * mb + a_head_lo;
+        const int head = HSTRIDE * mb + a_head;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           if (t < L) {
@@ -235,23 +186,32 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         }
       }
     }
+    // folded head weights w*q_scale of the item's rows, staged once in LDS
+    // with coalesced loads, then 16 per block into registers
+    for (int i = tid; i < C::RW * H; i += NT) {
+      const int t = t0 + i / H, head = i % H;
+      float v = 0.f;
+      if (t < L) {
+        v = bf16_to_f32(p.w[(size_t)t * H + head]);
+        if (p.q_scale) v *= p.q_scale[(size_t)t * p.qs_row + (size_t)head * p.qs_head];
+      }
+      sh.weff[i] = v;
+    }
+    __syncthreads();
     float wr[C::MB][16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int t = t0 + wave * C::QPW + kh * C::QPH + j / C::HB;
+      const int slot = C::SPLIT ? 0 : kh * C::QPH + j / C::HB;
+      const int row = wave * C::QPW + slot;
 #pragma unroll
       for (int mb = 0; mb < C::MB; ++mb) {
-        const int head = 16 * mb + j % C::HB;
-        float v = 0.f;
-        if (t < L) {
-          v = bf16_to_f32(p.w[(size_t)t * H + head]);
-          if (p.q_scale) v *= p.q_scale[(size_t)t * p.qs_row + (size_t)head * p.qs_head];
-        }
-        wr[mb][j] = v;
+        const int head = C::SPLIT ? 32 * mb + 8 * (j >> 2) + 4 * kh + (j & 3) : j % C::HB;
+        wr[mb][j] = sh.weff[row * H + head];
       }
     }
-    const int row_base = wave * C::QPW + kh * C::QPH;   // local row of slot r is row_base + r
+    const int row_base = wave * C::QPW + (C::SPLIT ? 0 : kh * C::QPH);   // local row of slot r is row_base + r
     float* smp_lane = smp + (size_t)row_base * p.sample_m + col;
+    float* smp_row = smp + (size_t)wave * p.sample_m;   // H >= 32: the wave's single row
 
     // ---- key tile staging.  Loads are unconditional: keys past the end read
     // the last key (such keys are always masked), so no branch merges into
@@ -265,7 +225,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int key = min(kt + ci / (C::ROWB / 16), L - 1);
         gbuf[c] = *reinterpret_cast<const v4i*>(p.k + (size_t)key * C::ROWB + (ci % (C::ROWB / 16)) * 16);
       }
-      gks = p.k_scale ? p.k_scale[min(kt + (tid & (TK - 1)), L - 1)] : 1.f;
+      gks = p.k_scale ? p.k_scale[min(kt + (tid & (C::TK - 1)), L - 1)] : 1.f;
     };
     auto lstore = [&](int buf) {
 #pragma unroll
@@ -276,34 +236,108 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
           *reinterpret_cast<v4i*>(&sh.ktile[buf][kl * C::STRIDE + (ci % (C::ROWB / 16)) * 16]) = gbuf[c];
         }
       }
-      if (tid < TK) sh.kscale[buf][tid] = gks;
+      if (tid < C::TK) {
+        // H >= 32 reads k_scale lane-major: key 64*pair + lane at lane*(TK/64) + pair
+        const int slot = C::SPLIT ? (tid % 64) * (C::TK / 64) + tid / 64 : tid;
+        sh.kscale[buf][slot] = gks;
+      }
     };
 
-    // ---- scores of this lane's key column of subtile `sub` of LDS tile `buf`
-    auto subtile_scores = [&](int buf, int sub, float (&score)[C::QPH]) {
-      const uint8_t* bp = &sh.ktile[buf][(32 * sub + col) * C::STRIDE + kh * (C::ROWB / 2)];
-      OT b[C::KS];
+    // ---- scores of all four 32-key subtiles of LDS tile `buf`.  One
+    // straight-line block: two accumulators alternate between the 32-head
+    // blocks so the MFMAs of block i+1 run while the VALU epilogue of block i
+    // executes, and the B operand of the next subtile is fetched from LDS
+    // during the current one.
+    //   H <= 16: on_score(sub, score[QPH]) per subtile; lane (half, col) holds
+    //            key 32*sub + col of its half's query slots.
+    //   H >= 32: on_score(pair, score) per subtile pair; the halves trade
+    //            partial head sums so that lane l holds the full score of key
+    //            64*pair + l (half 0 finishes the even subtile, half 1 the odd).
+    auto tile_scores = [&](int buf, auto&& on_score) {
+      const uint8_t* bp = &sh.ktile[buf][col * C::STRIDE + kh * (C::ROWB / 2)];
+      constexpr int NSUB = C::TK / 32;
+      constexpr int STEPS = NSUB * C::MB;
+      OT b[2][C::KS];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) b[ks] = load_opnd<C::FP8>(bp + ks * C::SB);
-      // head-weighted ReLU sum, in-lane; one 32-head block at a time so that
-      // the epilogue of block mb overlaps the MFMAs of block mb+1
+      for (int ks = 0; ks < C::KS; ++ks) b[0][ks] = load_opnd<C::FP8>(bp + ks * C::SB);
+      v16f acc[2];
       float part[C::QPH][4];
+      float even_half = 0.f;   // H >= 32: this half's partial sum of the even subtile
+      // H >= 32: k_scale of key 64*pair + lane for every pair of the tile
+      // (stored lane-major, one vector read)
+      float ksc_v[C::TK / 64];
+      if constexpr (C::SPLIT) {
+        const float* kp = &sh.kscale[buf][lane * (C::TK / 64)];
+        if constexpr (C::TK == 256) {
+          const float4 v = *reinterpret_cast<const float4*>(kp);
+          ksc_v[0] = v.x; ksc_v[1] = v.y; ksc_v[2] = v.z; ksc_v[3] = v.w;
+        } else {
+          const float2 v = *reinterpret_cast<const float2*>(kp);
+          ksc_v[0] = v.x; ksc_v[1] = v.y;
+        }
+      }
+      auto epilogue = [&](int step) {
+        const int sub = step / C::MB, mb = step % C::MB;
+        const v16f& a = acc[step & 1];
+        if (mb == 0) {
 #pragma unroll
-      for (int r = 0; r < C::QPH; ++r)
+          for (int r = 0; r < C::QPH; ++r)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) part[r][u] = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < C::MB; ++mb) {
-        v16f acc = v16f{};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) acc = mma<C::FP8>(qa[mb][ks], b[ks], acc);
+            for (int u = 0; u < 4; ++u) part[r][u] = 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-          part[j / C::HB][j & 3] = fmaf(wr[mb][j], fmaxf(acc[j], 0.f), part[j / C::HB][j & 3]);
-      }
-      const float ksc = sh.kscale[buf][32 * sub + col];
+          part[C::slot_of(j)][j & 3] = fmaf(wr[mb][j], fmaxf(a[j], 0.f), part[C::slot_of(j)][j & 3]);
+        if (mb == C::MB - 1) {
+          if constexpr (C::SPLIT) {
+            const float h = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
+            if ((sub & 1) == 0) {
+              even_half = h;
+            } else {
+              // v_permlane32_swap(X = even partials, Y = odd partials) returns
+              // (X[l], X[l+32]) to lanes l < 32 and (Y[l-32], Y[l]) to lanes
+              // l >= 32: the two partials of key 64*pair + l, half 0 first
+              const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(even_half), __float_as_uint(h),
+                                                                false, false);
+              const float full = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+              on_score(sub >> 1, full * ksc_v[sub >> 1]);
+            }
+          } else {
+            const float ksc = sh.kscale[buf][32 * sub + col];
+            float score[C::QPH];
 #pragma unroll
-      for (int r = 0; r < C::QPH; ++r) score[r] = ((part[r][0] + part[r][1]) + (part[r][2] + part[r][3])) * ksc;
+            for (int r = 0; r < C::QPH; ++r)
+              score[r] = ((part[r][0] + part[r][1]) + (part[r][2] + part[r][3])) * ksc;
+            on_score(sub, score);
+          }
+        }
+      };
+#pragma unroll
+      for (int step = 0; step < STEPS; ++step) {
+        const int sub = step / C::MB, mb = step % C::MB;
+        if (mb == 0 && sub + 1 < NSUB) {
+#pragma unroll
+          for (int ks = 0; ks < C::KS; ++ks)
+            b[(sub + 1) & 1][ks] = load_opnd<C::FP8>(bp + 32 * (sub + 1) * C::STRIDE + ks * C::SB);
+        }
+        v16f c = v16f{};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) c = mma<C::FP8>(qa[mb][ks], b[sub & 1][ks], c);
+        acc[step & 1] = c;
+        if (step > 0) epilogue(step - 1);
+        // Issue order inside one step: each MFMA is followed by its share of
+        // the previous block's epilogue, which only reads the other
+        // accumulator, so VALU work runs while the matrix core is busy.  The
+        // barrier keeps steps apart (hoisting the MFMAs of later steps would
+        // run out of registers).
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (32 + C::KS - 1) / C::KS, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      epilogue(STEPS - 1);
     };
 
     // A work item runs once with a threshold estimated from a key sample and,
@@ -313,13 +347,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       // key tiles below t0 (valid for every row of the item) into LDS; their
       // scores give a conservative estimate tau0 of each row's k-th score.
       // The remaining iterations stream the causal prefix in key order.
-      const int smp_tiles = (attempt == 0 && t0 >= 4 * p.topk) ? min(p.sample_m / TK, t0 / (8 * TK)) : 0;
+      const int smp_tiles = (attempt == 0 && t0 >= 4 * p.topk) ? min(p.sample_m / C::TK, t0 / (8 * C::TK)) : 0;
       const int stile = smp_tiles >= 4 ? smp_tiles : 0;
-      const int stride = stile ? (t0 / stile) / TK * TK : 0;
+      const int stride = stile ? (t0 / stile) / C::TK * C::TK : 0;
       const int total = stile + ntiles;
-      auto tile_key = [&](int i) { return i < stile ? i * stride : (i - stile) * TK; };
+      auto tile_key = [&](int i) { return i < stile ? i * stride : (i - stile) * C::TK; };
 
-      float tau0[C::QPH];   // sample threshold (inclusive), -inf without a sample
+      float tau0[C::QPH];   // sample threshold, -inf without a sample
       int cnt[C::QPH];      // list length of each of this lane's rows (uniform in the lane half)
       int scnt[C::QPH];     // entries staged in LDS during the current tile
       float tau[C::QPH];    // k-th best score after the last compaction (-inf before)
@@ -341,74 +375,112 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int buf = it & 1;
         if (it + 1 < total) gload(tile_key(it + 1));
 
+        // The two branches run the same MFMA sequence; the distinct markers
+        // keep the compiler from hoisting it into the common predecessor,
+        // where its results would stay live across the branch.
+        // rows past the end of the sequence accept nothing
+        float thr[C::QPH];
 #pragma unroll
-        for (int sub = 0; sub < TK / 32; ++sub) {
-          const int s0 = kt + 32 * sub;
-          if (sampling || s0 < kend) {
-            float sc[C::QPH];
-            subtile_scores(buf, sub, sc);
-            const int s = s0 + col;
-            if (sampling) {
+        for (int r = 0; r < C::QPH; ++r)
+          thr[r] = (t0 + row_base + r < L) ? fmaxf(tau[r], tau0[r]) : __builtin_inff();
+        if (sampling) {
+          asm volatile("; sample tile" ::: "memory");
+          if constexpr (C::SPLIT) {
+            tile_scores(buf, [&](int pair, float sc) { smp_row[it * C::TK + 64 * pair + lane] = sc; });
+          } else {
+            tile_scores(buf, [&](int sub, const float (&sc)[C::QPH]) {
 #pragma unroll
-              for (int r = 0; r < C::QPH; ++r) smp_lane[r * p.sample_m + it * TK + 32 * sub] = sc[r];
-            } else {
+              for (int r = 0; r < C::QPH; ++r) smp_lane[r * p.sample_m + it * C::TK + 32 * sub] = sc[r];
+            });
+          }
+        } else {
+          asm volatile("; stream tile" ::: "memory");
+          // Branch-free staging: passing lanes take the next free slots of the
+          // row's stage in key order, the others fill the slots after them
+          // (overwritten by the next group), so every group of keys writes
+          // consecutive words.  Filter: strictly above max(tau, tau0).
+          if constexpr (C::SPLIT) {
+            const int tr = t0 + wave;
+            tile_scores(buf, [&](int pair, float score) {
+              const int s = kt + 64 * pair + lane;
+              if constexpr (DENSE) {
+                if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)tr * L + s] = s <= tr ? score : -__builtin_inff();
+              }
+              const bool pass = (s <= tr) && (score > thr[0]);
+              const uint64_t m = ballot64(pass);
+              const int np = __popcll(m);
+              const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+              const int pos = scnt[0] + (pass ? before : np + lane - before);
+              sh.stage_sc[wave][pos] = score;
+              sh.stage_ix[wave][pos] = s;
+              scnt[0] += np;
+            });
+          } else {
+            tile_scores(buf, [&](int sub, const float (&sc)[C::QPH]) {
+              const int s = kt + 32 * sub + col;
+              const uint32_t lt = (1u << col) - 1u;
 #pragma unroll
               for (int r = 0; r < C::QPH; ++r) {
                 const float score = sc[r];
                 const int tr = t0 + row_base + r;
-                const bool valid = (s <= tr) && (tr < L);
                 if constexpr (DENSE) {
-                  if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)tr * L + s] = valid ? score : -__builtin_inff();
+                  if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)tr * L + s] = s <= tr ? score : -__builtin_inff();
                 }
-                // tau: strict (later keys lose ties to the kept ones); tau0: inclusive
-                const bool pass = valid && score > tau[r] && score >= tau0[r];
+                const bool pass = (s <= tr) && (score > thr[r]);
                 const uint64_t m = ballot64(pass);
                 const uint32_t mh = kh ? (uint32_t)(m >> 32) : (uint32_t)m;
-                if (pass) {
-                  const int pos = scnt[r] + __popc(mh & ((1u << col) - 1u));
-                  sh.stage_sc[row_base + r][pos] = score;
-                  sh.stage_ix[row_base + r][pos] = s;
-                }
-                scnt[r] += __popc(mh);
+                const int np = __popc(mh);
+                const int before = __popc(mh & lt);
+                const int pos = scnt[r] + (pass ? before : np + col - before);
+                sh.stage_sc[row_base + r][pos] = score;
+                sh.stage_ix[row_base + r][pos] = s;
+                scnt[r] += np;
               }
-            }
+            });
           }
         }
 
         if (!sampling) {
-          // ---- move this tile's staged candidates to the rows' lists (one burst per row)
+          // ---- move this tile's staged candidates to the rows' lists (one
+          // burst per row); a list without room for one more tile is
+          // compacted to its k best right away by the wave that owns it
+          wave_lds_sync();   // stage entries were written by other lanes
 #pragma unroll
           for (int rr = 0; rr < C::QPW; ++rr) {
-            const int hf = rr / C::QPH, r = rr % C::QPH;
+            const int hf = C::SPLIT ? 0 : rr / C::QPH, r = C::SPLIT ? 0 : rr % C::QPH;
             const int n = __builtin_amdgcn_readlane(scnt[r], hf * 32);
             const int c0 = __builtin_amdgcn_readlane(cnt[r], hf * 32);
             const int row = wave * C::QPW + rr;
+            float* rs = wsc + (size_t)row * p.cap;
+            int* ri = wix + (size_t)row * p.cap;
             for (int e = lane; e < n; e += 64) {
-              wsc[(size_t)row * p.cap + c0 + e] = sh.stage_sc[row][e];
-              wix[(size_t)row * p.cap + c0 + e] = sh.stage_ix[row][e];
+              rs[c0 + e] = sh.stage_sc[row][e];
+              ri[c0 + e] = sh.stage_ix[row][e];
             }
+            int c = c0 + n;
+            if (c + C::TK > p.cap) {
+              __threadfence_block();
+              float tnew;
+              c = wave_select(rs, ri, c, p.topk, rs, ri, 0, sh.whist[wave], &tnew);
+              if (C::SPLIT || kh == hf) tau[r] = tnew;
+            }
+            if (C::SPLIT || kh == hf) cnt[r] = c;
           }
 #pragma unroll
-          for (int r = 0; r < C::QPH; ++r) {
-            cnt[r] += scnt[r];
-            scnt[r] = 0;
-            // room for one more tile in every list, else ask for a compaction
-            if (col == 0 && cnt[r] + TK > p.cap) {
-              sh.row_cnt[row_base + r] = cnt[r];
-              atomicOr(&sh.need_mask, 1u << (row_base + r));
-            }
-          }
+          for (int r = 0; r < C::QPH; ++r) scnt[r] = 0;
         }
         if (it + 1 < total) lstore(buf ^ 1);
         __syncthreads();
         if (it == stile - 1) {
           // k' = expected sample count above the row's k-th score + 4.5 sigma:
           // the k'-th sample score is below the true k-th score except with
-          // probability ~1e-5, and the end-of-item check catches that case.
-          const int m = stile * TK;
+          // probability ~1e-5.  Any threshold is safe: a row whose list ends
+          // with at least min(k, t+1) keys strictly above it holds every key
+          // of its top k, and the end-of-item check redoes any other row.
+          const int m = stile * C::TK;
 #pragma unroll
           for (int rr = 0; rr < C::QPW; ++rr) {
-            const int hf = rr / C::QPH, r = rr % C::QPH;
+            const int hf = C::SPLIT ? 0 : rr / C::QPH, r = C::SPLIT ? 0 : rr % C::QPH;
             const int t = t0 + wave * C::QPW + rr;
             const float pk = (float)p.topk / (float)(t + 1);
             const float mu = (float)m * pk;
@@ -419,31 +491,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
                   wave_kth_key(smp + (size_t)(wave * C::QPW + rr) * p.sample_m, m, kp, sh.whist[wave]);
               v = key_to_float(key);
             }
-            if (kh == hf) tau0[r] = v;
+            if (C::SPLIT || kh == hf) tau0[r] = v;
           }
-          __syncthreads();
-        }
-        const uint32_t mask = sh.need_mask;
-        if (mask) {
-          for (int rl = 0; rl < C::RW; ++rl) {
-            if ((mask >> rl) & 1u) {
-              float* rs = wsc + (size_t)rl * p.cap;
-              int* ri = wix + (size_t)rl * p.cap;
-              const int n = block_select<NT>(rs, ri, sh.row_cnt[rl], p.topk, rs, ri, 0, sh.sel, lsc, lix,
-                                             &sh.row_tau[rl]);
-              if (tid == 0) sh.row_cnt[rl] = n;
-              __syncthreads();
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < C::QPH; ++r) {
-            if ((mask >> (row_base + r)) & 1u) {
-              cnt[r] = sh.row_cnt[row_base + r];
-              tau[r] = sh.row_tau[row_base + r];
-            }
-          }
-          __syncthreads();
-          if (tid == 0) sh.need_mask = 0u;
           __syncthreads();
         }
       }
@@ -463,14 +512,16 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         continue;               // recompute the item without the sample threshold
       }
 
-      // ---- final selection, written to the output rows in ascending key order
-      for (int rl = 0; rl < C::RW; ++rl) {
-        const int t = t0 + rl;
-        if (t >= L) break;
+      // ---- final selection: each wave writes its own rows, in ascending key order
+#pragma unroll 1
+      for (int rr = 0; rr < C::QPW; ++rr) {
+        const int row = wave * C::QPW + rr;
+        const int t = t0 + row;
+        if (t >= L) continue;
         int* dix = p.out_idx + (size_t)t * p.topk;
         float* dsc = p.out_score ? p.out_score + (size_t)t * p.topk : nullptr;
-        block_select<NT>(wsc + (size_t)rl * p.cap, wix + (size_t)rl * p.cap, sh.row_cnt[rl], p.topk, dsc, dix,
-                         p.topk, sh.sel, lsc, lix, nullptr);
+        wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix, p.topk,
+                    sh.whist[wave], nullptr);
       }
       break;
     }
@@ -491,7 +542,7 @@ __global__ void prefill_prepare_kernel(int* counter, float* dense, long long n_d
 
 template <int DT, int H, int D, bool DENSE>
 static hipError_t launch_variant(const PrefillParams& p, int grid, hipStream_t stream) {
-  const size_t dyn = (size_t)p.cap * 8;
+  const size_t dyn = (size_t)PfCfg<DT, H, D>::RW * p.sample_m * sizeof(float);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DT, H, D, DENSE>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
@@ -504,65 +555,66 @@ static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t strea
   return p.out_dense ? launch_variant<DT, H, D, true>(p, grid, stream) : launch_variant<DT, H, D, false>(p, grid, stream);
 }
 
-template <int DT, int H, int D>
-static size_t static_lds() {
-  return sizeof(PfShared<DT, H, D>);
+// Every compiled (dtype, H, D) configuration.
+#define DSA_PF_CONFIGS(X)                                                          \
+  X(DSA_FP8_E4M3, 64, 128) X(DSA_FP8_E4M3, 64, 64) X(DSA_FP8_E4M3, 32, 128)        \
+  X(DSA_FP8_E4M3, 32, 64) X(DSA_FP8_E4M3, 16, 128) X(DSA_FP8_E4M3, 16, 64)         \
+  X(DSA_FP8_E4M3, 8, 128) X(DSA_FP8_E4M3, 8, 64) X(DSA_BF16, 64, 64)               \
+  X(DSA_BF16, 32, 128) X(DSA_BF16, 32, 64) X(DSA_BF16, 16, 128) X(DSA_BF16, 16, 64) \
+  X(DSA_BF16, 8, 128) X(DSA_BF16, 8, 64)
+
+struct PfInfo {
+  size_t static_lds;   // bytes of the kernel's static shared memory
+  int tile_keys;       // keys per LDS tile
+};
+
+static bool pf_info(int dt, int H, int D, PfInfo* out) {
+#define DSA_PF_INFO(DT_, H_, D_)                                                 \
+  if (dt == DT_ && H == H_ && D == D_) {                                         \
+    *out = PfInfo{sizeof(PfShared<DT_, H_, D_>), PfCfg<DT_, H_, D_>::TK};          \
+    return true;                                                                 \
+  }
+  DSA_PF_CONFIGS(DSA_PF_INFO)
+#undef DSA_PF_INFO
+  return false;
 }
 
-int prefill_rows_per_item(int H) { return WAVES * 2 * (H < 16 ? 16 / H : 1); }
+int prefill_rows_per_item(int H) { return H >= 32 ? WAVES : WAVES * 2 * (16 / H); }
 
 bool prefill_supported(int dt, int H, int D) {
-  const bool fp8 = dt == DSA_FP8_E4M3;
-  if (!(H == 8 || H == 16 || H == 32 || H == 64)) return false;
-  if (D != 64 && D != 128) return false;
-  if (!fp8 && H == 64 && D == 128) return false;   // register budget
-  return true;
+  PfInfo info;
+  return pf_info(dt, H, D, &info);
 }
-
-int prefill_tile_keys() { return TK; }
 
 // Keys per row sampled for the threshold estimate: the sampled scores of all
-// rows of a work item live in the dynamic LDS area (2 * cap words), at most
-// 1024 per row, whole tiles only; fewer than 4 tiles disables the sample.
-int prefill_sample_keys(int H, int cap) {
+// rows of a work item live in dynamic LDS next to the kernel's static shared
+// memory, at most 1024 per row, whole tiles only; fewer than 4 tiles disables
+// the sample.
+int prefill_sample_keys(int dt, int H, int D) {
+  PfInfo info;
+  if (!pf_info(dt, H, D, &info)) return 0;
+  const size_t lds_limit = 160 * 1024;
+  const int tk = info.tile_keys;
   const int rw = prefill_rows_per_item(H);
-  int m = (2 * cap / rw) / TK * TK;
+  if (info.static_lds >= lds_limit) return 0;
+  int m = (int)((lds_limit - info.static_lds) / ((size_t)rw * sizeof(float)));
+  m = m / tk * tk;
   if (m > 1024) m = 1024;
-  return m >= 4 * TK ? m : 0;
+  return m >= 4 * tk ? m : 0;
 }
 
-// Candidate list capacity per row: 4*topk when the LDS allows (the select
-// stages one list in LDS next to the kernel's static shared memory), never
-// less than topk plus one tile.  Returns 0 if no capacity fits.
+// Candidate list capacity per row (workspace memory): 4*topk, at least topk
+// plus 16 tiles, plus 2 tiles of slack, so that rows scored without a sample
+// threshold (fewer than 4*topk keys) never need a compaction.  0 when the
+// configuration is not built.
 int prefill_list_capacity(int dt, int H, int D, int topk) {
-  size_t st = 0;
-#define DSA_PF_LDS(DT_, H_, D_) \
-  if (dt == DT_ && H == H_ && D == D_) st = static_lds<DT_, H_, D_>();
-  DSA_PF_LDS(DSA_FP8_E4M3, 64, 128)
-  DSA_PF_LDS(DSA_FP8_E4M3, 64, 64)
-  DSA_PF_LDS(DSA_FP8_E4M3, 32, 128)
-  DSA_PF_LDS(DSA_FP8_E4M3, 32, 64)
-  DSA_PF_LDS(DSA_FP8_E4M3, 16, 128)
-  DSA_PF_LDS(DSA_FP8_E4M3, 16, 64)
-  DSA_PF_LDS(DSA_FP8_E4M3, 8, 128)
-  DSA_PF_LDS(DSA_FP8_E4M3, 8, 64)
-  DSA_PF_LDS(DSA_BF16, 64, 64)
-  DSA_PF_LDS(DSA_BF16, 32, 128)
-  DSA_PF_LDS(DSA_BF16, 32, 64)
-  DSA_PF_LDS(DSA_BF16, 16, 128)
-  DSA_PF_LDS(DSA_BF16, 16, 64)
-  DSA_PF_LDS(DSA_BF16, 8, 128)
-  DSA_PF_LDS(DSA_BF16, 8, 64)
-#undef DSA_PF_LDS
-  if (st == 0) return 0;
-  const size_t lds_limit = 160 * 1024;
-  if (st + 8 * (size_t)(topk + TK) > lds_limit) return 0;
+  PfInfo info;
+  if (!pf_info(dt, H, D, &info)) return 0;
+  const size_t tk = (size_t)info.tile_keys;
   size_t cap = 4 * (size_t)topk;
-  if (cap < (size_t)topk + 16 * TK) cap = (size_t)topk + 16 * TK;
-  const size_t max_cap = (lds_limit - st) / 8 / 64 * 64;
-  if (cap > max_cap) cap = max_cap;
-  cap = cap / 64 * 64;
-  if (cap < (size_t)topk + TK) return 0;
+  if (cap < (size_t)topk + 16 * tk) cap = (size_t)topk + 16 * tk;
+  cap += 2 * tk;
+  cap = (cap + 63) / 64 * 64;
   return (int)cap;
 }
 
@@ -572,21 +624,7 @@ hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid
   hipLaunchKernelGGL(prefill_prepare_kernel, dim3(pg), dim3(256), 0, stream, p.counter, p.out_dense, n_dense);
 #define DSA_PF_CASE(DT_, H_, D_) \
   if (dt == DT_ && H == H_ && D == D_) return launch_one<DT_, H_, D_>(p, grid, stream);
-  DSA_PF_CASE(DSA_FP8_E4M3, 64, 128)
-  DSA_PF_CASE(DSA_FP8_E4M3, 64, 64)
-  DSA_PF_CASE(DSA_FP8_E4M3, 32, 128)
-  DSA_PF_CASE(DSA_FP8_E4M3, 32, 64)
-  DSA_PF_CASE(DSA_FP8_E4M3, 16, 128)
-  DSA_PF_CASE(DSA_FP8_E4M3, 16, 64)
-  DSA_PF_CASE(DSA_FP8_E4M3, 8, 128)
-  DSA_PF_CASE(DSA_FP8_E4M3, 8, 64)
-  DSA_PF_CASE(DSA_BF16, 64, 64)
-  DSA_PF_CASE(DSA_BF16, 32, 128)
-  DSA_PF_CASE(DSA_BF16, 32, 64)
-  DSA_PF_CASE(DSA_BF16, 16, 128)
-  DSA_PF_CASE(DSA_BF16, 16, 64)
-  DSA_PF_CASE(DSA_BF16, 8, 128)
-  DSA_PF_CASE(DSA_BF16, 8, 64)
+  DSA_PF_CONFIGS(DSA_PF_CASE)
 #undef DSA_PF_CASE
   return hipErrorInvalidValue;
 }
