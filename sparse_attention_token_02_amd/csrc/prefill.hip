@@ -74,9 +74,14 @@ struct PfCfg {
   // 128 bytes (halves the per-tile barriers), else 128 (LDS budget)
   static constexpr int TK = (ROWB <= 128 && SPLIT) ? 256 : 128;
   static constexpr int RW = WAVES * QPW;            // query rows per work item
-  static constexpr int STRIDE = ROWB + 16;          // padded LDS row (bank-conflict free b128 reads)
-  static constexpr int CHUNKS = TK * ROWB / 16;     // 16-byte pieces of a key tile
-  static constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  // LDS key tile: rows of ROWB bytes, unpadded; the 16-byte chunks of row r
+  // sit at chunk position c ^ swz(r), swz(r) = (r / RPB) & (CPR - 1), so the
+  // 16 lanes that read one chunk of 16 consecutive rows in a ds_read_b128
+  // cycle hit 16 different 16-byte bank groups of the 64-bank LDS.
+  static constexpr int CPR = ROWB / 16;             // 16-byte chunks per key row
+  static constexpr int RPB = 256 / ROWB;            // key rows per 256-byte bank sweep
+  static constexpr int NLD = TK * ROWB / 1024;      // 1 KB direct-to-LDS loads per tile
+  static_assert(ROWB <= 256 && NLD % WAVES == 0, "tile layout");
   static_assert(H == 8 || H == 16 || H == 32 || H == 64, "unsupported head count");
   static_assert(D % KM == 0 && ROWB / 2 == KS * SB, "unsupported head dim");
   static_assert(RW <= 32, "row mask is 32 bits");
@@ -87,7 +92,7 @@ struct PfCfg {
 template <int DT, int H, int D>
 struct PfShared {
   using C = PfCfg<DT, H, D>;
-  uint8_t ktile[2][C::TK * C::STRIDE];     // double-buffered key tile
+  __attribute__((aligned(1024))) uint8_t ktile[2][C::TK * C::ROWB];   // double-buffered key tile (swizzled)
   __attribute__((aligned(16))) float kscale[2][C::TK];
   float stage_sc[C::RW][C::TK];            // this tile's accepted candidates, per row
   int stage_ix[C::RW][C::TK];
@@ -213,56 +218,85 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     float* smp_lane = smp + (size_t)row_base * p.sample_m + col;
     float* smp_row = smp + (size_t)wave * p.sample_m;   // H >= 32: the wave's single row
 
-    // ---- key tile staging.  Loads are unconditional: keys past the end read
-    // the last key (such keys are always masked), so no branch merges into
-    // gbuf and no early wait is forced on the prefetch.
-    v4i gbuf[C::CPT];
-    float gks = 1.f;
-    auto gload = [&](int kt) {
+    // ---- key tile staging: direct global -> LDS loads (no registers, no
+    // copy), 1 KB per wave instruction: lane i of load g fills chunk position
+    // 64g + i of the tile.  Keys past the end read the last key (always
+    // masked), so every load is unconditional.  Completion is awaited (vmcnt)
+    // right before the barrier that publishes the tile.
+    auto issue_tile = [&](int kt, int buf) {
 #pragma unroll
-      for (int c = 0; c < C::CPT; ++c) {
-        const int ci = min(tid + c * NT, C::CHUNKS - 1);
-        const int key = min(kt + ci / (C::ROWB / 16), L - 1);
-        gbuf[c] = *reinterpret_cast<const v4i*>(p.k + (size_t)key * C::ROWB + (ci % (C::ROWB / 16)) * 16);
+      for (int i = 0; i < C::NLD / WAVES; ++i) {
+        const int g = wave + WAVES * i;
+        const int pos = 64 * g + lane;
+        const int r = pos / C::CPR;
+        const int c = (pos % C::CPR) ^ ((r / C::RPB) & (C::CPR - 1));
+        const uint8_t* src = p.k + (size_t)min(kt + r, L - 1) * C::ROWB + c * 16;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)&sh.ktile[buf][1024 * g], 16, 0, 0);
       }
-      gks = p.k_scale ? p.k_scale[min(kt + (tid & (C::TK - 1)), L - 1)] : 1.f;
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int c = 0; c < C::CPT; ++c) {
-        const int ci = tid + c * NT;
-        if (ci < C::CHUNKS) {
-          const int kl = ci / (C::ROWB / 16);
-          *reinterpret_cast<v4i*>(&sh.ktile[buf][kl * C::STRIDE + (ci % (C::ROWB / 16)) * 16]) = gbuf[c];
+      if (wave < C::TK / 64) {
+        // H >= 32 reads k_scale lane-major: key 64*pair + lane at lane*(TK/64) + pair
+        const int pos = 64 * wave + lane;
+        const int kk = C::SPLIT ? 64 * (pos % (C::TK / 64)) + pos / (C::TK / 64) : pos;
+        if (p.k_scale) {
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(p.k_scale + min(kt + kk, L - 1)),
+                                           (__attribute__((address_space(3))) void*)&sh.kscale[buf][64 * wave], 4, 0, 0);
+        } else {
+          sh.kscale[buf][pos] = 1.f;
         }
       }
-      if (tid < C::TK) {
-        // H >= 32 reads k_scale lane-major: key 64*pair + lane at lane*(TK/64) + pair
-        const int slot = C::SPLIT ? (tid % 64) * (C::TK / 64) + tid / 64 : tid;
-        sh.kscale[buf][slot] = gks;
-      }
     };
+    // this lane's B-operand chunk offsets within a key row (the swizzle only
+    // depends on the row modulo 32, i.e. on the lane)
+    const int bswz = (col / C::RPB) & (C::CPR - 1);
+    int boff[C::KS][C::FP8 ? 2 : 1];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int h = 0; h < (C::FP8 ? 2 : 1); ++h)
+        boff[ks][h] = ((((kh * (C::ROWB / 2) + ks * C::SB) >> 4) + h) ^ bswz) * 16;
 
-    // ---- scores of all four 32-key subtiles of LDS tile `buf`.  One
-    // straight-line block: two accumulators alternate between the 32-head
-    // blocks so the MFMAs of block i+1 run while the VALU epilogue of block i
-    // executes, and the B operand of the next subtile is fetched from LDS
-    // during the current one.
+    // ---- scores of all 32-key subtiles of LDS tile `buf`.  One straight-line
+    // block: two accumulator sets alternate between subtiles so the MFMAs of
+    // subtile i+1 run while the VALU epilogue of subtile i executes, and the
+    // B operand of the next subtile is fetched from LDS during the current one.
     //   H <= 16: on_score(sub, score[QPH]) per subtile; lane (half, col) holds
     //            key 32*sub + col of its half's query slots.
     //   H >= 32: on_score(pair, score) per subtile pair; the halves trade
     //            partial head sums so that lane l holds the full score of key
     //            64*pair + l (half 0 finishes the even subtile, half 1 the odd).
     auto tile_scores = [&](int buf, auto&& on_score) {
-      const uint8_t* bp = &sh.ktile[buf][col * C::STRIDE + kh * (C::ROWB / 2)];
+      const uint8_t* bp = &sh.ktile[buf][col * C::ROWB];
+      auto load_b = [&](int sub, int ks) -> OT {
+        const uint8_t* rp = bp + 32 * sub * C::ROWB;
+        if constexpr (C::FP8) {
+          const v4i lo = *reinterpret_cast<const v4i*>(rp + boff[ks][0]);
+          const v4i hi = *reinterpret_cast<const v4i*>(rp + boff[ks][C::FP8 ? 1 : 0]);
+          return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
+          return __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(rp + boff[ks][0]));
+        }
+      };
       constexpr int NSUB = C::TK / 32;
-      constexpr int STEPS = NSUB * C::MB;
-      OT b[2][C::KS];
+      // B operands, three subtiles deep: the buffer refilled for subtile
+      // i+1 was last read by the MFMAs of subtile i-2, long complete, so the
+      // refill never waits on an MFMA still reading its registers
+      OT b[3][C::KS];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) b[0][ks] = load_opnd<C::FP8>(bp + ks * C::SB);
-      v16f acc[2];
+      for (int ks = 0; ks < C::KS; ++ks) b[0][ks] = load_b(0, ks);
+      v16f acc[2][C::MB];
       float part[C::QPH][4];
       float even_half = 0.f;   // H >= 32: this half's partial sum of the even subtile
+      // Each finished score is handed to on_score one subtile later, so its
+      // dependent filter chain issues between the next subtile's MFMAs.
+      float pend_sc[C::QPH];
+      int pend_id = -1;
+      auto flush_pending = [&]() {
+        if (pend_id >= 0) {
+          if constexpr (C::SPLIT) on_score(pend_id, pend_sc[0]);
+          else on_score(pend_id, pend_sc);
+        }
+      };
       // H >= 32: k_scale of key 64*pair + lane for every pair of the tile
       // (stored lane-major, one vector read)
       float ksc_v[C::TK / 64];
@@ -276,68 +310,83 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
           ksc_v[0] = v.x; ksc_v[1] = v.y;
         }
       }
-      auto epilogue = [&](int step) {
-        const int sub = step / C::MB, mb = step % C::MB;
-        const v16f& a = acc[step & 1];
-        if (mb == 0) {
+      // epilogue of subtile `sub` (its accumulators for every head block)
+      auto epilogue = [&](int sub) {
+        const v16f* a = acc[sub & 1];
+#pragma unroll
+        for (int r = 0; r < C::QPH; ++r)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) part[r][u] = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            part[C::slot_of(j)][j & 3] = fmaf(wr[mb][j], fmaxf(a[mb][j], 0.f), part[C::slot_of(j)][j & 3]);
+        if constexpr (C::SPLIT) {
+          const float h = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
+          if ((sub & 1) == 0) {
+            even_half = h;
+          } else {
+            // v_permlane32_swap(X = even partials, Y = odd partials) returns
+            // (X[l], X[l+32]) to lanes l < 32 and (Y[l-32], Y[l]) to lanes
+            // l >= 32: the two partials of key 64*pair + l, half 0 first
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(even_half), __float_as_uint(h),
+                                                              false, false);
+            const float full = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+            pend_sc[0] = full * ksc_v[sub >> 1];
+            pend_id = sub >> 1;
+          }
+        } else {
+          const float ksc = sh.kscale[buf][32 * sub + col];
 #pragma unroll
           for (int r = 0; r < C::QPH; ++r)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) part[r][u] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          part[C::slot_of(j)][j & 3] = fmaf(wr[mb][j], fmaxf(a[j], 0.f), part[C::slot_of(j)][j & 3]);
-        if (mb == C::MB - 1) {
-          if constexpr (C::SPLIT) {
-            const float h = (part[0][0] + part[0][1]) + (part[0][2] + part[0][3]);
-            if ((sub & 1) == 0) {
-              even_half = h;
-            } else {
-              // v_permlane32_swap(X = even partials, Y = odd partials) returns
-              // (X[l], X[l+32]) to lanes l < 32 and (Y[l-32], Y[l]) to lanes
-              // l >= 32: the two partials of key 64*pair + l, half 0 first
-              const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(even_half), __float_as_uint(h),
-                                                                false, false);
-              const float full = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-              on_score(sub >> 1, full * ksc_v[sub >> 1]);
-            }
-          } else {
-            const float ksc = sh.kscale[buf][32 * sub + col];
-            float score[C::QPH];
-#pragma unroll
-            for (int r = 0; r < C::QPH; ++r)
-              score[r] = ((part[r][0] + part[r][1]) + (part[r][2] + part[r][3])) * ksc;
-            on_score(sub, score);
-          }
+            pend_sc[r] = ((part[r][0] + part[r][1]) + (part[r][2] + part[r][3])) * ksc;
+          pend_id = sub;
         }
       };
+      // MFMAs of one subtile are issued K-step-major across the head blocks,
+      // so an MFMA never waits on the one issued just before it; each is
+      // followed by its share of the previous subtile's epilogue, which only
+      // reads the other accumulator set.  The barrier keeps subtiles apart
+      // (hoisting later MFMAs would run out of registers).
+      constexpr int NMF = C::MB * C::KS;
+      constexpr int VPER = (32 * C::MB + 24 + NMF - 1) / NMF;
+      constexpr int NDS = C::KS * (C::FP8 ? 2 : 1);   // ds_read_b128 per subtile B operand
 #pragma unroll
-      for (int step = 0; step < STEPS; ++step) {
-        const int sub = step / C::MB, mb = step % C::MB;
-        if (mb == 0 && sub + 1 < NSUB) {
+      for (int sub = 0; sub < NSUB; ++sub) {
+        if (sub + 1 < NSUB) {
 #pragma unroll
           for (int ks = 0; ks < C::KS; ++ks)
-            b[(sub + 1) & 1][ks] = load_opnd<C::FP8>(bp + 32 * (sub + 1) * C::STRIDE + ks * C::SB);
+            b[(sub + 1) % 3][ks] = load_b(sub + 1, ks);
         }
-        v16f c = v16f{};
+        v16f c[C::MB];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) c = mma<C::FP8>(qa[mb][ks], b[sub & 1][ks], c);
-        acc[step & 1] = c;
-        if (step > 0) epilogue(step - 1);
-        // Issue order inside one step: each MFMA is followed by its share of
-        // the previous block's epilogue, which only reads the other
-        // accumulator, so VALU work runs while the matrix core is busy.  The
-        // barrier keeps steps apart (hoisting the MFMAs of later steps would
-        // run out of registers).
+        for (int mb = 0; mb < C::MB; ++mb) c[mb] = v16f{};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int mb = 0; mb < C::MB; ++mb) c[mb] = mma<C::FP8>(qa[mb][ks], b[sub % 3][ks], c[mb]);
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) acc[sub & 1][mb] = c[mb];
+        if (sub > 0) {
+          flush_pending();
+          pend_id = -1;
+          epilogue(sub - 1);
+        }
+        // next subtile's B reads first, then MFMAs each followed by a share
+        // of the epilogue
+        if (sub + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, (32 + C::KS - 1) / C::KS, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      epilogue(STEPS - 1);
+      flush_pending();
+      pend_id = -1;
+      epilogue(NSUB - 1);
+      flush_pending();
     };
 
     // A work item runs once with a threshold estimated from a key sample and,
@@ -365,15 +414,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         tau[r] = -__builtin_inff();
       }
 
-      gload(tile_key(0));
-      lstore(0);
+      issue_tile(tile_key(0), 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
 
       for (int it = 0; it < total; ++it) {
         const int kt = tile_key(it);
         const bool sampling = it < stile;
         const int buf = it & 1;
-        if (it + 1 < total) gload(tile_key(it + 1));
+        if (it + 1 < total) issue_tile(tile_key(it + 1), buf ^ 1);
 
         // The two branches run the same MFMA sequence; the distinct markers
         // keep the compiler from hoisting it into the common predecessor,
@@ -469,7 +518,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
           for (int r = 0; r < C::QPH; ++r) scnt[r] = 0;
         }
-        if (it + 1 < total) lstore(buf ^ 1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's part of the next tile has landed
         __syncthreads();
         if (it == stile - 1) {
           // k' = expected sample count above the row's k-th score + 4.5 sigma:
