@@ -288,3 +288,20 @@ def fs_layer_inputs(cfg: dict, layer: int, rows=None, with_keys: bool = True) ->
     W = fs_noise_rows(cfg, "w", layer, rows, H) / _F32(cfg["w_div"])
     out["w"] = bf16_bits(W.astype(np.float32))
     return out
+
+
+def fs_keys_by_layer(cfg: dict, last_layer: int):
+    """Yields (layer, k codes [L,D] uint8, k_scale [L] float32) for layers
+    0..last_layer of the layer-reuse workload, carrying the key recurrence
+    forward instead of restarting it for every layer (same values as
+    ``fs_layer_inputs(cfg, layer)["k"]``)."""
+    L, D = cfg["L"], cfg["D"]
+    idx = np.arange(L, dtype=np.uint64)[:, None] * np.uint64(D) + np.arange(D, dtype=np.uint64)[None, :]
+    rho, sigma = _F32(cfg["rho"]), _F32(cfg["sigma"])
+    X = normal_f32(cfg["seed"], _sid("k", 0), idx)
+    for layer in range(last_layer + 1):
+        if layer > 0:
+            N = normal_f32(cfg["seed"], _sid("k", layer), idx)
+            X = ((rho * X).astype(np.float32) + (sigma * N).astype(np.float32)).astype(np.float32)
+        codes, scales = quant_rows_e4m3(X)
+        yield layer, codes, scales
