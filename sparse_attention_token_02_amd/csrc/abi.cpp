@@ -177,10 +177,11 @@ dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t
 
 // ---------------------------------------------------------------------------
 
-// Decode workspace: score rows [B, ld] fp32, histograms [B, 4096], counters
-// [B, 2], selected lists [B, topk], candidate keys and indices [B, Lmax] each.
+// Decode workspace: score rows [B, ld] fp32, per-workgroup histograms,
+// selection bitmaps, candidate keys and indices [B, Lmax] each, candidate
+// counts and the per-sequence cut (bin of the k-th score, keys above it).
 struct DecodeWs {
-  size_t scores, hist, counts, sel, ckey, cidx, total;
+  size_t scores, hist, bitmap, ckey, cidx, ccnt, cut, total;
   int ld;
 };
 
@@ -191,15 +192,18 @@ static DecodeWs decode_ws(int B, int Lmax, int topk) {
   w.scores = off;
   off += align_up((size_t)B * w.ld * 4, 256);
   w.hist = off;
-  off += align_up((size_t)B * dsa::decode_hist_bins() * 4, 256);
-  w.counts = off;
-  off += align_up((size_t)B * 2 * 4, 256);
-  w.sel = off;
-  off += align_up((size_t)B * topk * 4, 256);
+  const dsa::DecodeWsSizes z = dsa::decode_ws_sizes(Lmax);
+  off += align_up((size_t)B * z.hist_words * 4, 256);
+  w.bitmap = off;
+  off += align_up((size_t)B * z.bitmap_words * 4, 256);
   w.ckey = off;
   off += align_up((size_t)B * Lmax * 4, 256);
   w.cidx = off;
   off += align_up((size_t)B * Lmax * 4, 256);
+  w.ccnt = off;
+  off += align_up((size_t)B * z.cand_cnt * 4, 256);
+  w.cut = off;
+  off += align_up((size_t)B * 8, 256);
   w.total = off;
   return w;
 }
@@ -245,10 +249,11 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
   p.ld = lay.ld;
   p.scores = reinterpret_cast<float*>(base + lay.scores);
   p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
-  p.counts = reinterpret_cast<int*>(base + lay.counts);
-  p.sel_idx = reinterpret_cast<int*>(base + lay.sel);
   p.cand_key = reinterpret_cast<uint32_t*>(base + lay.ckey);
   p.cand_idx = reinterpret_cast<int*>(base + lay.cidx);
+  p.bitmap = reinterpret_cast<uint32_t*>(base + lay.bitmap);
+  p.cand_cnt = reinterpret_cast<int*>(base + lay.ccnt);
+  p.cut = reinterpret_cast<int2*>(base + lay.cut);
   hipError_t e = dsa::decode_launch(p, H, D, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return ok();

@@ -8,24 +8,22 @@
 // and the min(k, len_b) best keys (score descending, index ascending) are
 // written in ascending key order, padded with -1.
 //
-// Four launches:
-// 1. decode_prepare_kernel clears the per-sequence histograms and counters.
-// 2. decode_score_kernel streams the fp8 cache once.  A wave reads 32 whole
+// Two launches:
+// 1. decode_score_kernel streams the fp8 cache once.  A wave reads 32 whole
 //    consecutive keys per step with 16-byte loads and keeps four steps in
 //    flight.  Each lane owns one key column and the D/2 contiguous bytes of
 //    its half of that key; fp8 is widened to bf16 exactly (e4m3 is a subset of
 //    bf16) and the contraction runs on v_mfma_f32_32x32x16_bf16 with the heads
 //    on the MFMA row dimension (q stays in registers).  The per-token fp32
 //    scale multiplies the fp32 score (folding it into the bf16 operand would
-//    not be exact).  Scores go to a workspace row, and a 4096-bin histogram of
-//    the top 12 bits of their order-preserving keys is accumulated per
-//    sequence.
-// 3. decode_classify_kernel (many workgroups per sequence) finds the bin of
-//    the k-th score from the histogram, lists every key of a higher bin as
-//    selected, and every key of that bin as a candidate.
-// 4. decode_finalize_kernel (one workgroup per sequence) picks the remaining
-//    keys among the candidates (radix select, ties to the lower index) and
-//    writes the selection in ascending key order through an LDS bitmap.
+//    not be exact).  Scores go to a workspace row, and each workgroup stores
+//    its own 4096-bin histogram of the top 12 bits of their order-preserving
+//    keys (whole, so nothing has to be cleared beforehand).
+// 2. decode_select_kernel (one workgroup per sequence) sums those histograms,
+//    finds the bin of the k-th score, marks every key of a higher bin in an
+//    LDS bitmap and collects the keys of that bin as candidates in one pass
+//    over the scores, resolves the candidates by radix select (ties to the
+//    lower index), and writes the marked keys in ascending order.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -37,12 +35,17 @@ constexpr int DS_NT = 256;          // score kernel threads
 constexpr int DS_NSUB = 64;         // 32-key steps per wave
 constexpr int DS_PF = 4;            // steps in flight per wave
 constexpr int DS_KPB = (DS_NT / 64) * DS_NSUB * 32;   // keys per workgroup
-constexpr int HBINS = 4096;
-constexpr int CL_NT = 256;          // classify threads
-constexpr int CL_PER_THREAD = 32;   // scores per classify thread (8 x float4)
-constexpr int CL_CHUNK = CL_NT * CL_PER_THREAD;
-constexpr int FN_NT = 1024;         // finalize threads
-constexpr int FN_CAP = 8192;        // candidates held in LDS by the finalize kernel
+constexpr int DS_MAXWG = 32;        // score workgroups per sequence at most (Lmax <= 262144)
+constexpr int HBINS = 4096;         // fine bins: top 12 bits of the order-preserving key
+constexpr int CBINS = 256;          // coarse bins: top 8 bits
+constexpr int FPC = HBINS / CBINS;  // fine bins per coarse bin
+constexpr int PW = HBINS / 2 + CBINS / 2;   // words of one score workgroup's packed histograms
+constexpr int SL_NT = 1024;         // select threads
+constexpr int SL_SLICE = 16384;     // scores per select workgroup
+constexpr int SL_MAXG = 16;         // select workgroups per sequence at most (Lmax <= 262144)
+constexpr int SL_CAP = 8192;        // candidate slots in LDS in the finalize kernel
+constexpr int SL_SPEC = SL_CAP / SL_MAXG;   // candidates per slice read speculatively
+constexpr int SL_MAXW = SL_MAXG * SL_SLICE / 32;   // bitmap words per sequence at most
 
 // two e4m3 (bytes 2*HI, 2*HI+1 of src) -> two bf16, exact
 template <bool HI>
@@ -53,41 +56,6 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t src) {
 
 __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
   return min(max(p.lens[b], 0), p.Lmax);   // lengths outside [0, Lmax] are clamped
-}
-
-// Bin of the k-th score: sum the histogram from the top.  Every thread of the
-// block ends with (d*, count above d*) in bc[0..1].  NT threads, HBINS/NT bins each.
-template <int NT>
-__device__ void kth_bin(const uint32_t* gh, int k, int* wtot, int* bc) {
-  constexpr int PER = HBINS / NT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t h[PER];
-  int s = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    h[i] = gh[PER * tid + i];
-    s += (int)h[i];
-  }
-  // exclusive suffix sum over threads (sum of bins above this thread's bins)
-  int incl = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_down(incl, o);
-    if (lane + o < 64) incl += t;
-  }
-  if (lane == 0) wtot[wave] = incl;
-  __syncthreads();
-  int above = incl - s;
-  for (int w = wave + 1; w < NT / 64; ++w) above += wtot[w];
-#pragma unroll
-  for (int i = PER - 1; i >= 0; --i) {
-    if (above < k && above + (int)h[i] >= k) {
-      bc[0] = PER * tid + i;
-      bc[1] = above;
-    }
-    above += (int)h[i];
-  }
-  __syncthreads();
 }
 
 }  // namespace
@@ -105,8 +73,16 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
 
   const int b = blockIdx.y;
   const int len = seq_len(p, b);
-  const int kbase = blockIdx.x * DS_KPB;
-  if (kbase >= len) return;
+  // Interleaved key mapping: step `sub` of wave w of workgroup x reads the
+  // 32-key chunk (sub * nwg + x) * WAVES + w, so at any moment the workgroups
+  // of a sequence sweep one contiguous region of its cache together.
+  constexpr int WAVES = DS_NT / 64;
+  const int nwg = gridDim.x;
+  const int x = blockIdx.x;
+  const int nchunk = (len + 31) >> 5;
+  if (WAVES * x >= nchunk) return;
+  // steps this workgroup needs (whole prefetch groups)
+  const int nstep = min(DS_NSUB, ((nchunk - WAVES * x + WAVES * nwg - 1) / (WAVES * nwg) + DS_PF - 1) / DS_PF * DS_PF);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -117,7 +93,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   const uint8_t* cache_b = p.cache + (size_t)b * p.Lmax * D;
   const float* ks_b = p.k_scale + (size_t)b * p.Lmax;
   float* sc_b = p.scores + (size_t)b * p.ld;
-  const int wbase = kbase + wave * DS_NSUB * 32;
+  auto chunk_key = [&](int sub) { return 32 * ((sub * nwg + x) * WAVES + wave); };
 
   // q and w first: every later wait for them then leaves the cache prefetches
   // (issued after them) in flight
@@ -158,7 +134,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
     kss[slot] = ks_b[s];
   };
 #pragma unroll
-  for (int u = 0; u < DS_PF; ++u) fetch(u, wbase + 32 * u);
+  for (int u = 0; u < DS_PF; ++u) fetch(u, chunk_key(u));
 
   for (int i = tid; i < HBINS; i += DS_NT) hist[i] = 0u;
   __syncthreads();
@@ -166,17 +142,17 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // the ring is unrolled inside a rolled loop; with unconditional loads every
   // slot keeps its registers across iterations
 #pragma unroll 1
-  for (int g = 0; g < DS_NSUB; g += DS_PF) {
+  for (int g = 0; g < nstep; g += DS_PF) {
 #pragma unroll
     for (int u = 0; u < DS_PF; ++u) {
       const int sub = g + u;
-      const int s0 = wbase + 32 * sub;
+      const int s0 = chunk_key(sub);
       {
         v4i cur[NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i) cur[i] = raw[u][i];
         const float cks = kss[u];
-        fetch(u, min(s0 + 32 * DS_PF, wbase + 32 * (DS_NSUB - 1)));   // past the end: harmless reload
+        fetch(u, chunk_key(min(sub + DS_PF, nstep - 1)));   // past the end: harmless reload
 
         // widen 16 fp8 of a load into two 8-element bf16 operands
         v8bf bop[KS];
@@ -207,146 +183,78 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
         const float score = tot * cks;
         const int s = s0 + col;
         if (kh == 0 && s < len) {
-          sc_stage[s - kbase] = score;
+          sc_stage[sub * (32 * WAVES) + wave * 32 + col] = score;
           atomicAdd(&hist[ordered_key(score) >> 20], 1u);
         }
       }
     }
   }
   __syncthreads();
-  // score rows are 64-float aligned (ld), kbase is a multiple of 64
-  const int nval = min(DS_KPB, len - kbase);
-  for (int i = tid; 4 * i < nval; i += DS_NT) {
-    if (4 * i + 3 < nval) {
-      reinterpret_cast<v4i*>(sc_b + kbase)[i] = reinterpret_cast<const v4i*>(sc_stage)[i];
+  // each step wrote 32*WAVES consecutive keys; score rows are 64-float
+  // aligned (ld), so the 16-byte stores are aligned
+  for (int i = tid; i < nstep * 8 * WAVES; i += DS_NT) {
+    const int sub = i / (8 * WAVES), q4 = i % (8 * WAVES);
+    const int s = 32 * WAVES * (sub * nwg + x) + 4 * q4;
+    const v4i v = reinterpret_cast<const v4i*>(sc_stage)[i];
+    if (s + 3 < len) {
+      *reinterpret_cast<v4i*>(sc_b + s) = v;
     } else {
-      for (int e = 4 * i; e < nval; ++e) sc_b[kbase + e] = sc_stage[e];
-    }
-  }
-  uint32_t* gh = p.hist + (size_t)b * HBINS;
-  for (int i = tid; i < HBINS; i += DS_NT) {
-    const uint32_t v = hist[i];
-    if (v) atomicAdd(&gh[i], v);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// classify: keys above the k-th bin are selected, keys in it are candidates
-// ---------------------------------------------------------------------------
-
-__global__ void __launch_bounds__(CL_NT) decode_classify_kernel(DecodeParams p) {
-  __shared__ int wtot[CL_NT / 64];
-  __shared__ int bc[2];
-  __shared__ int ws_sel[CL_NT / 64], ws_cand[CL_NT / 64];
-  __shared__ int base_sel, base_cand;
-  const int b = blockIdx.y;
-  const int n = seq_len(p, b);
-  const int k = p.topk;
-  const int c0 = blockIdx.x * CL_CHUNK;
-  if (n <= k || c0 >= n) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* sc = p.scores + (size_t)b * p.ld;
-
-  // all of this thread's scores in flight at once
-  float v[CL_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < CL_PER_THREAD / 4; ++i) {
-    const int j = c0 + 4 * (tid + i * CL_NT);
-    v4i x = v4i{0, 0, 0, 0};
-    if (j + 3 < n) {
-      x = *reinterpret_cast<const v4i*>(sc + j);
-    } else {
-#pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (j + e < n) x[e] = __float_as_int(sc[j + e]);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[4 * i + e] = __int_as_float(x[e]);
-  }
-  kth_bin<CL_NT>(p.hist + (size_t)b * HBINS, k, wtot, bc);
-  const uint32_t dstar = (uint32_t)bc[0];
-
-  int nsel = 0, ncand = 0;
-#pragma unroll
-  for (int i = 0; i < CL_PER_THREAD; ++i) {
-    const int j = c0 + 4 * (tid + (i >> 2) * CL_NT) + (i & 3);
-    const uint32_t dg = ordered_key(v[i]) >> 20;
-    nsel += (j < n && dg > dstar);
-    ncand += (j < n && dg == dstar);
-  }
-  // one atomic per workgroup and list
-  int s_incl = nsel, c_incl = ncand;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a = __shfl_up(s_incl, o), c = __shfl_up(c_incl, o);
-    if (lane >= o) {
-      s_incl += a;
-      c_incl += c;
+        if (s + e < len) sc_b[s + e] = __int_as_float(v[e]);
     }
   }
-  if (lane == 63) {
-    ws_sel[wave] = s_incl;
-    ws_cand[wave] = c_incl;
+  // this workgroup's histograms, stored whole as 16-bit counts (a workgroup
+  // scores at most DS_KPB < 65536 keys): no atomics, nothing to clear.
+  // Words [0, HBINS/2): the fine bins in pairs; [HBINS/2, PW): the coarse
+  // bins (sums of FPC consecutive fine bins) in pairs.
+  uint32_t* gh = p.hist + ((size_t)b * nwg + x) * PW;
+  for (int i = tid; i < HBINS / 8; i += DS_NT) {
+    const v4i lo = reinterpret_cast<const v4i*>(hist)[2 * i];
+    const v4i hi = reinterpret_cast<const v4i*>(hist)[2 * i + 1];
+    reinterpret_cast<v4i*>(gh)[i] = v4i{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), hi[0] | (hi[1] << 16),
+                                        hi[2] | (hi[3] << 16)};
   }
-  __syncthreads();
-  int s_pre = s_incl - nsel, c_pre = c_incl - ncand, s_tot = 0, c_tot = 0;
+  for (int i = tid; i < CBINS / 2; i += DS_NT) {
+    uint32_t c[2] = {0u, 0u};
 #pragma unroll
-  for (int w = 0; w < CL_NT / 64; ++w) {
-    s_pre += (w < wave) ? ws_sel[w] : 0;
-    c_pre += (w < wave) ? ws_cand[w] : 0;
-    s_tot += ws_sel[w];
-    c_tot += ws_cand[w];
-  }
-  if (tid == 0) {
-    base_sel = s_tot ? atomicAdd(&p.counts[2 * b], s_tot) : 0;
-    base_cand = c_tot ? atomicAdd(&p.counts[2 * b + 1], c_tot) : 0;
-  }
-  __syncthreads();
-  int* sel = p.sel_idx + (size_t)b * p.topk;
-  uint32_t* ckey = p.cand_key + (size_t)b * p.Lmax;
-  int* cidx = p.cand_idx + (size_t)b * p.Lmax;
-  int ps = base_sel + s_pre, pc = base_cand + c_pre;
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-  for (int i = 0; i < CL_PER_THREAD; ++i) {
-    const int j = c0 + 4 * (tid + (i >> 2) * CL_NT) + (i & 3);
-    const uint32_t key = ordered_key(v[i]);
-    const uint32_t dg = key >> 20;
-    if (j < n && dg > dstar) {
-      sel[ps++] = j;
-    } else if (j < n && dg == dstar) {
-      ckey[pc] = key;
-      cidx[pc] = j;
-      ++pc;
-    }
+      for (int q = 0; q < FPC / 4; ++q) {
+        const v4i t = reinterpret_cast<const v4i*>(hist)[(2 * i + h) * (FPC / 4) + q];
+        c[h] += (uint32_t)(t[0] + t[1] + t[2] + t[3]);
+      }
+    gh[HBINS / 2 + i] = c[0] | (c[1] << 16);
   }
 }
 
 // ---------------------------------------------------------------------------
-// finalize: exact choice among the candidates, ascending output
+// select: the classify kernel finds the bin of the k-th score and sorts each
+// slice of SL_SLICE scores into selected keys and candidates; the finalize
+// kernel resolves the candidates and writes the ascending top-k
 // ---------------------------------------------------------------------------
 
 namespace {
 
-struct FinShared {
-  int wtot[FN_NT / 64];
+static_assert(DS_KPB < 65536, "16-bit partial histograms");
+
+struct SelShared {
+  uint32_t hist[HBINS];               // sequence histogram of the top 12 key bits
   uint32_t hist8[256];
+  int wtot[SL_NT / 64];
+  int coff[SL_MAXG + 1];              // candidate offsets of the slices
   int bc[4];
+  int ncand;
 };
 
 // exclusive scan of v over the workgroup; *total gets the sum
-__device__ int fn_scan(int v, FinShared& sh, int* total) {
+__device__ int sl_scan(int v, SelShared& sh, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
+  const int incl = wave_incl_sum(v);
   if (lane == 63) sh.wtot[wave] = incl;
   __syncthreads();
   int pre = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < FN_NT / 64; ++w) {
+  for (int w = 0; w < SL_NT / 64; ++w) {
     const int x = sh.wtot[w];
     pre += (w < wave) ? x : 0;
     tot += x;
@@ -358,93 +266,297 @@ __device__ int fn_scan(int v, FinShared& sh, int* total) {
 
 }  // namespace
 
-__global__ void __launch_bounds__(FN_NT) decode_finalize_kernel(DecodeParams p) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ FinShared sh;
-  const int b = blockIdx.x;
-  const int tid = threadIdx.x;
+__global__ void __launch_bounds__(SL_NT) decode_classify_kernel(DecodeParams p, int nwg) {
+  __shared__ SelShared sh;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = seq_len(p, b);
   const int k = p.topk;
   int* out = p.out_idx + (size_t)b * k;
   float* osc = p.out_score ? p.out_score + (size_t)b * k : nullptr;
   const float* sc = p.scores + (size_t)b * p.ld;
 
-  if (n <= k) {
-    for (int j = tid; j < k; j += FN_NT) {
-      out[j] = j < n ? j : -1;
-      if (osc) osc[j] = j < n ? sc[j] : -__builtin_inff();
-    }
+  if (n <= k) {                       // every key is kept
+    if (g == 0)
+      for (int j = tid; j < k; j += SL_NT) {
+        out[j] = j < n ? j : -1;
+        if (osc) osc[j] = j < n ? sc[j] : -__builtin_inff();
+      }
     return;
   }
-  const int nw = (p.Lmax + 31) >> 5;
-  uint32_t* bm = dyn;                 // selected keys
-  uint32_t* tb = dyn + nw;            // keys tied with the k-th score
-  uint32_t* lkey = dyn + 2 * nw;      // candidate keys (when they fit)
-  for (int i = tid; i < 2 * nw; i += FN_NT) dyn[i] = 0u;
-  const int n_sel = p.counts[2 * b];
-  const int m = p.counts[2 * b + 1];
-  int need = k - n_sel;                // keys still to take from the candidates (>= 1)
-  const uint32_t* gkey = p.cand_key + (size_t)b * p.Lmax;
-  const int* gidx = p.cand_idx + (size_t)b * p.Lmax;
-  const bool in_lds = m <= FN_CAP;
-  if (in_lds)
-    for (int c = tid; c < m; c += FN_NT) lkey[c] = gkey[c];
-  __syncthreads();
-  const int* sel = p.sel_idx + (size_t)b * p.topk;
-  for (int i = tid; i < n_sel; i += FN_NT) {
-    const int j = sel[i];
-    atomicOr(&bm[j >> 5], 1u << (j & 31));
-  }
-  const uint32_t* keys = in_lds ? lkey : gkey;
+  const int nslice = (n + SL_SLICE - 1) / SL_SLICE;
+  if (g >= nslice) return;
+  const int nwmax = (p.Lmax + 31) >> 5;
+  uint32_t* gbm = p.bitmap + (size_t)b * nwmax;
+  uint32_t* gkey = p.cand_key + (size_t)b * p.Lmax;
+  int* gidx = p.cand_idx + (size_t)b * p.Lmax;
 
-  // exact k-th key among the candidates: they share the top 12 bits
-  uint32_t prefix = m ? keys[0] & 0xFFF00000u : 0u;
-  uint32_t pmask = 0xFFF00000u;
-  for (int bit = 19; bit >= 0;) {
-    const int nb = bit + 1 < 8 ? bit + 1 : 8;
-    const int shift = bit + 1 - nb;
-    const uint32_t dm = (1u << nb) - 1u;
-    for (int i = tid; i < 256; i += FN_NT) sh.hist8[i] = 0u;
+  // 1. the coarse histograms of the active score workgroups (those that had
+  //    keys), then this slice's scores (a float4 per lane and load, 256
+  //    consecutive scores per wave and load; the row holds at least 4 nq
+  //    floats): loads complete in issue order, so the histogram work below
+  //    does not wait for the scores
+  const int nchunk = (n + 31) >> 5;
+  const int nact = min(nwg, (nchunk + DS_NT / 64 - 1) / (DS_NT / 64));
+  const uint32_t* ph = p.hist + (size_t)b * nwg * PW;
+  constexpr int CW = CBINS / 2;       // coarse words per partial
+  constexpr int PS = SL_NT / CW;      // partials read side by side
+  constexpr int CU = (DS_MAXWG + PS - 1) / PS;
+  uint32_t ct[CU];
+#pragma unroll
+  for (int u = 0; u < CU; ++u) ct[u] = ph[(size_t)min(tid / CW + PS * u, nact - 1) * PW + HBINS / 2 + tid % CW];
+  const int s0 = g * SL_SLICE;
+  const int nq = (n + 3) >> 2;
+  constexpr int SU = SL_SLICE / (4 * SL_NT);
+  v4f v[SU];
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    const int gi = (SL_NT / 64) * u + wave;
+    v[u] = reinterpret_cast<const v4f*>(sc)[min((s0 >> 2) + 64 * gi + lane, nq - 1)];
+  }
+  {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int u = 0; u < CU; ++u)
+      if (tid / CW + PS * u < nact) {
+        lo += ct[u] & 0xFFFFu;
+        hi += ct[u] >> 16;
+      }
+    if (tid < CBINS) sh.hist[tid] = 0u;
+    if (tid < FPC) sh.hist8[tid] = 0u;
+    if (tid == 0) sh.ncand = 0;
     __syncthreads();
-    for (int c = tid; c < m; c += FN_NT) {
-      const uint32_t key = keys[c];
-      if ((key & pmask) == prefix) atomicAdd(&sh.hist8[(key >> shift) & dm], 1u);
-    }
+    if (lo) atomicAdd(&sh.hist[2 * (tid % CW)], lo);
+    if (hi) atomicAdd(&sh.hist[2 * (tid % CW) + 1], hi);
     __syncthreads();
-    const int hv = tid < 256 ? (int)sh.hist8[tid] : 0;
-    int t2;
-    const int pre = fn_scan(hv, sh, &t2);
-    const int ab = t2 - pre - hv;      // entries in higher bins
-    if (tid < 256 && ab < need && ab + hv >= need) {
+  }
+
+  // 2. bin d* of the k-th score and the number of keys above it: first the
+  //    coarse bin, then its FPC fine bins (read from the partials only there)
+  {
+    const int hv = tid < CBINS ? (int)sh.hist[tid] : 0;
+    int tot;
+    const int pre = sl_scan(hv, sh, &tot);
+    const int ab = tot - pre - hv;     // keys in higher coarse bins
+    if (tid < CBINS && ab < k && ab + hv >= k) {
       sh.bc[0] = tid;
       sh.bc[1] = ab;
     }
     __syncthreads();
-    prefix |= (uint32_t)sh.bc[0] << shift;
-    pmask |= dm << shift;
-    need -= sh.bc[1];
-    bit -= nb;
+    const int cstar = sh.bc[0];
+    if (tid < (FPC / 2) * nact) {
+      const uint32_t t = ph[(size_t)(tid / (FPC / 2)) * PW + (FPC / 2) * cstar + tid % (FPC / 2)];
+      if (t & 0xFFFFu) atomicAdd(&sh.hist8[2 * (tid % (FPC / 2))], t & 0xFFFFu);
+      if (t >> 16) atomicAdd(&sh.hist8[2 * (tid % (FPC / 2)) + 1], t >> 16);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int h = lane < FPC ? (int)sh.hist8[lane] : 0;
+      int incl = h;                     // keys in fine bins lane.. of the coarse bin
+#pragma unroll
+      for (int o = 1; o < FPC; o <<= 1) {
+        const int t = __shfl_down(incl, o);
+        if (lane + o < FPC) incl += t;
+      }
+      const int ab2 = sh.bc[1] + incl - h;
+      if (lane < FPC && ab2 < k && ab2 + h >= k) {
+        sh.bc[2] = FPC * cstar + lane;
+        sh.bc[3] = ab2;
+      }
+    }
     __syncthreads();
   }
-  const uint32_t kstar = prefix;
-  for (int c = tid; c < m; c += FN_NT) {
-    const uint32_t key = keys[c];
-    const int j = gidx[c];
-    if (key > kstar) atomicOr(&bm[j >> 5], 1u << (j & 31));
-    else if (key == kstar) atomicOr(&tb[j >> 5], 1u << (j & 31));
+  const uint32_t dstar = (uint32_t)sh.bc[2];
+
+  // 3. classify the slice: keys of higher bins are marked in the global
+  //    bitmap (eight lanes OR their four bits into one word), keys of bin d*
+  //    go to this slice's candidate region
+  {
+    uint32_t cnd[SU];
+    uint32_t key[SU][4];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+      const int j0 = s0 + 256 * ((SL_NT / 64) * u + wave) + 4 * lane;
+      uint32_t selb = 0;
+      cnd[u] = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = j0 + e < n;
+        key[u][e] = ordered_key(v[u][e]);
+        const uint32_t dg = key[u][e] >> 20;
+        selb |= (uint32_t)(valid && dg > dstar) << e;
+        cnd[u] |= (uint32_t)(valid && dg == dstar) << e;
+      }
+      uint32_t word = selb << (4 * (lane & 7));
+      word |= (uint32_t)__shfl_xor((int)word, 1);
+      word |= (uint32_t)__shfl_xor((int)word, 2);
+      word |= (uint32_t)__shfl_xor((int)word, 4);
+      if ((lane & 7) == 0 && j0 < n) gbm[j0 >> 5] = word;
+    }
+    // compaction: one LDS atomic per wave
+    uint64_t me[SU][4];
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < SU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        me[u][e] = ballot64((cnd[u] >> e) & 1u);
+        tot += __popcll(me[u][e]);
+      }
+    if (tot) {                        // uniform
+      int c0 = 0;
+      if (lane == 0) c0 = atomicAdd(&sh.ncand, tot);
+      c0 = __shfl(c0, 0);
+#pragma unroll
+      for (int u = 0; u < SU; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((cnd[u] >> e) & 1u) {
+            const int c = c0 + lanes_below(me[u][e]);
+            gkey[s0 + c] = key[u][e];
+            gidx[s0 + c] = s0 + 256 * ((SL_NT / 64) * u + wave) + 4 * lane + e;
+          }
+          c0 += __popcll(me[u][e]);
+        }
+    }
   }
   __syncthreads();
+  if (tid == 0) {
+    p.cand_cnt[(size_t)b * SL_MAXG + g] = sh.ncand;
+    if (g == 0) p.cut[b] = int2{(int)dstar, sh.bc[3]};
+  }
+}
 
-  // ties: the `need` lowest indices
-  const int wpt = (nw + FN_NT - 1) / FN_NT;   // words per thread, contiguous
+// One workgroup per sequence, after the classify kernel: resolve the k-th
+// score among the candidates and write the ascending top-k.
+__global__ void __launch_bounds__(SL_NT) decode_finalize_kernel(DecodeParams p) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ SelShared sh;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = seq_len(p, b);
+  const int k = p.topk;
+  if (n <= k) return;                 // written by the classify kernel
+  int* out = p.out_idx + (size_t)b * k;
+  float* osc = p.out_score ? p.out_score + (size_t)b * k : nullptr;
+  const float* sc = p.scores + (size_t)b * p.ld;
+  const int nslice = (n + SL_SLICE - 1) / SL_SLICE;
+  const int nwmax = (p.Lmax + 31) >> 5;
+  const uint32_t* gbm = p.bitmap + (size_t)b * nwmax;
+  const uint32_t* gkey = p.cand_key + (size_t)b * p.Lmax;
+  const int* gidx = p.cand_idx + (size_t)b * p.Lmax;
+  const int2 cut = p.cut[b];
+  const uint32_t dstar = (uint32_t)cut.x;
+
+  // 4. one round of loads: the bitmap, the candidate counts, and the first
+  //    SL_SPEC entries of every slice's candidate region (a count above
+  //    SL_SPEC, which is rare, sends every pass below to global memory)
+  const int nw = (n + 31) >> 5;       // bitmap words
+  uint32_t* bm = dyn;                 // selected keys
+  uint32_t* tb = dyn + nw;            // keys tied with the k-th score
+  uint32_t* lkey = dyn + 2 * nw;      // slice x's first entries at x * SL_SPEC
+  int* lidx = reinterpret_cast<int*>(lkey + SL_CAP);
   {
+    // every load is issued before any result is stored
+    constexpr int BR = SL_MAXW / SL_NT;           // bitmap words per thread at most
+    constexpr int CR = SL_CAP / SL_NT;            // candidate slots per thread
+    const int cnt = tid < nslice ? p.cand_cnt[(size_t)b * SL_MAXG + tid] : 0;
+    uint32_t bw[BR], ck[CR];
+    int cx[CR];
+#pragma unroll
+    for (int r = 0; r < BR; ++r) bw[r] = gbm[min(tid + SL_NT * r, nw - 1)];
+#pragma unroll
+    for (int r = 0; r < CR; ++r) {
+      const int c = tid + SL_NT * r;
+      const int e = min((c / SL_SPEC) * SL_SLICE + c % SL_SPEC, p.Lmax - 1);
+      if (c < nslice * SL_SPEC) {
+        ck[r] = gkey[e];
+        cx[r] = gidx[e];
+      }
+    }
+    if (tid < nslice) sh.coff[tid] = cnt;
+#pragma unroll
+    for (int r = 0; r < BR; ++r)
+      if (tid + SL_NT * r < nw) {
+        bm[tid + SL_NT * r] = bw[r];
+        tb[tid + SL_NT * r] = 0u;
+      }
+#pragma unroll
+    for (int r = 0; r < CR; ++r)
+      if (tid + SL_NT * r < nslice * SL_SPEC) {
+        lkey[tid + SL_NT * r] = ck[r];
+        lidx[tid + SL_NT * r] = cx[r];
+      }
+    if (tid == 0) sh.ncand = 0;       // ties with the k-th key
+    __syncthreads();
+  }
+  bool spill = false;
+  for (int x = 0; x < nslice; ++x) spill |= sh.coff[x] > SL_SPEC;
+  // calls body(key, index) for every candidate
+  auto for_cand = [&](auto body) {
+    if (!spill) {
+      for (int c = tid; c < nslice * SL_SPEC; c += SL_NT)
+        if (c % SL_SPEC < sh.coff[c / SL_SPEC]) body(lkey[c], lidx[c]);
+    } else {
+      for (int x = 0; x < nslice; ++x)
+        for (int i = tid; i < sh.coff[x]; i += SL_NT) body(gkey[x * SL_SLICE + i], gidx[x * SL_SLICE + i]);
+    }
+  };
+
+  // 5. exact k-th key among the candidates (they share the top 12 bits):
+  //    two rounds of 1024 bins, one per thread
+  int need = k - cut.y;               // keys still to take from bin d* (>= 1)
+  uint32_t prefix = dstar << 20;
+  uint32_t pmask = 0xFFF00000u;
+  static_assert(SL_NT == 1024, "one radix bin per thread");
+#pragma unroll 1
+  for (int shift = 10; shift >= 0; shift -= 10) {
+    sh.hist[tid] = 0u;
+    __syncthreads();
+    for_cand([&](uint32_t key, int) {
+      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 1023u], 1u);
+    });
+    __syncthreads();
+    const int hv = (int)sh.hist[tid];
+    int t2;
+    const int pre = sl_scan(hv, sh, &t2);
+    const int ab = t2 - pre - hv;      // entries in higher bins
+    if (ab < need && ab + hv >= need) {
+      sh.bc[2] = tid;
+      sh.bc[3] = ab;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sh.bc[2] << shift;
+    pmask |= 1023u << shift;
+    need -= sh.bc[3];
+  }
+  const uint32_t kstar = prefix;
+  for_cand([&](uint32_t key, int j) {
+    if (key > kstar) {
+      atomicOr(&bm[j >> 5], 1u << (j & 31));
+    } else if (key == kstar) {
+      atomicOr(&tb[j >> 5], 1u << (j & 31));
+      atomicAdd(&sh.ncand, 1);
+    }
+  });
+  __syncthreads();
+
+  // 6. ties with the k-th score: when more than `need` keys tie, the `need`
+  //    lowest indices (otherwise every tied key is taken)
+  const int wpt = (nw + SL_NT - 1) / SL_NT;   // bitmap words per thread, contiguous
+  if (sh.ncand == need) {             // uniform
+    for (int i = 0; i < wpt; ++i) {
+      const int wd = tid * wpt + i;
+      if (wd < nw) bm[wd] |= tb[wd];
+    }
+  } else {
     int c = 0;
     for (int i = 0; i < wpt; ++i) {
       const int wd = tid * wpt + i;
       if (wd < nw) c += __popc(tb[wd]);
     }
     int t3;
-    int before = fn_scan(c, sh, &t3);
+    int before = sl_scan(c, sh, &t3);
     for (int i = 0; i < wpt; ++i) {
       const int wd = tid * wpt + i;
       if (wd >= nw) break;
@@ -457,9 +569,8 @@ __global__ void __launch_bounds__(FN_NT) decode_finalize_kernel(DecodeParams p) 
       }
     }
   }
-  __syncthreads();
 
-  // write the selection in ascending key order
+  // 7. the selection in ascending key order (each thread's words are its own)
   {
     int c = 0;
     for (int i = 0; i < wpt; ++i) {
@@ -467,7 +578,7 @@ __global__ void __launch_bounds__(FN_NT) decode_finalize_kernel(DecodeParams p) 
       if (wd < nw) c += __popc(bm[wd]);
     }
     int t4;
-    int pos = fn_scan(c, sh, &t4);
+    int pos = sl_scan(c, sh, &t4);
     for (int i = 0; i < wpt; ++i) {
       const int wd = tid * wpt + i;
       if (wd >= nw) break;
@@ -486,38 +597,40 @@ __global__ void __launch_bounds__(FN_NT) decode_finalize_kernel(DecodeParams p) 
   }
 }
 
-__global__ void decode_prepare_kernel(uint32_t* hist, int nh, int* counts, int nc) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nh; i += gridDim.x * blockDim.x) hist[i] = 0u;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nc; i += gridDim.x * blockDim.x) counts[i] = 0;
-}
-
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
-size_t decode_finalize_lds_bytes(int Lmax) {
+static int score_workgroups(int Lmax) { return (Lmax + DS_KPB - 1) / DS_KPB; }
+static int select_workgroups(int Lmax) { return (Lmax + SL_SLICE - 1) / SL_SLICE; }
+
+size_t decode_select_lds_bytes(int Lmax) {
   const size_t nw = ((size_t)Lmax + 31) / 32;
-  return (2 * nw + (size_t)FN_CAP) * sizeof(uint32_t);
+  return 2 * nw * sizeof(uint32_t) + (size_t)SL_CAP * (sizeof(uint32_t) + sizeof(int));
 }
 
 bool decode_supported(int H, int D, int Lmax) {
   if (!(H == 16 || H == 32 || H == 64)) return false;
   if (D != 64 && D != 128) return false;
-  return decode_finalize_lds_bytes(Lmax) <= 150 * 1024;
+  if (select_workgroups(Lmax) > SL_MAXG || score_workgroups(Lmax) > DS_MAXWG) return false;
+  return decode_select_lds_bytes(Lmax) + sizeof(SelShared) <= 160 * 1024;
 }
 
-int decode_hist_bins() { return HBINS; }
+DecodeWsSizes decode_ws_sizes(int Lmax) {
+  DecodeWsSizes z;
+  z.hist_words = (size_t)score_workgroups(Lmax) * PW;
+  z.bitmap_words = ((size_t)Lmax + 31) / 32;
+  z.cand_cnt = SL_MAXG;
+  return z;
+}
 
 template <int H, int D>
 static void launch_score(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid((p.Lmax + DS_KPB - 1) / DS_KPB, p.B);
+  dim3 grid(score_workgroups(p.Lmax), p.B);
   hipLaunchKernelGGL((decode_score_kernel<H, D>), grid, dim3(DS_NT), 0, stream, p);
 }
 
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream) {
-  const int nh = p.B * HBINS;
-  const int pg = (nh + 255) / 256 < 1024 ? (nh + 255) / 256 : 1024;
-  hipLaunchKernelGGL(decode_prepare_kernel, dim3(pg), dim3(256), 0, stream, p.hist, nh, p.counts, 2 * p.B);
   if (H == 64 && D == 128) launch_score<64, 128>(p, stream);
   else if (H == 64 && D == 64) launch_score<64, 64>(p, stream);
   else if (H == 32 && D == 128) launch_score<32, 128>(p, stream);
@@ -527,15 +640,15 @@ hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_classify_kernel, dim3((p.Lmax + CL_CHUNK - 1) / CL_CHUNK, p.B), dim3(CL_NT), 0, stream,
-                     p);
+  hipLaunchKernelGGL(decode_classify_kernel, dim3(select_workgroups(p.Lmax), p.B), dim3(SL_NT), 0, stream, p,
+                     score_workgroups(p.Lmax));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = decode_finalize_lds_bytes(p.Lmax);
+  const size_t lds = decode_select_lds_bytes(p.Lmax);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_finalize_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_finalize_kernel, dim3(p.B), dim3(FN_NT), lds, stream, p);
+  hipLaunchKernelGGL(decode_finalize_kernel, dim3(p.B), dim3(SL_NT), lds, stream, p);
   return hipGetLastError();
 }
 

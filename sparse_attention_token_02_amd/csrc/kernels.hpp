@@ -44,11 +44,16 @@ struct DecodeParams {
   float* out_score;          // [B, topk], nullable
   int ld;                    // row stride of the score rows (Lmax rounded up to 64)
   float* scores;             // workspace [B, ld]
-  uint32_t* hist;            // workspace [B, 4096]
-  int* counts;               // workspace [B, 2]: selected, candidates
-  int* sel_idx;              // workspace [B, topk]
+  uint32_t* hist;            // workspace [B, hist_words]: per-workgroup 16-bit histograms
+  uint32_t* bitmap;          // workspace [B, bitmap_words]: selected keys
   uint32_t* cand_key;        // workspace [B, Lmax]
   int* cand_idx;             // workspace [B, Lmax]
+  int* cand_cnt;             // workspace [B, cand_cnt]: candidates per select workgroup
+  int2* cut;                 // workspace [B]: bin of the k-th score, keys in higher bins
+};
+
+struct DecodeWsSizes {
+  size_t hist_words, bitmap_words, cand_cnt;
 };
 
 struct OverlapParams {
@@ -71,8 +76,8 @@ hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid
 
 // decode.hip
 bool decode_supported(int H, int D, int Lmax);
-size_t decode_finalize_lds_bytes(int Lmax);
-int decode_hist_bins();
+size_t decode_select_lds_bytes(int Lmax);
+DecodeWsSizes decode_ws_sizes(int Lmax);
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream);
 
 // overlap.hip

@@ -108,3 +108,51 @@ def test_decode_128k_full_size_sampled_sequences(dsa, ragged):
     for b in range(cfg["B"]):
         v = idx[b][idx[b] >= 0]
         assert len(v) == min(cfg["topk"], lens[b]) and np.all(np.diff(v) > 0) and v[-1] < lens[b]
+
+
+def test_decode_reused_dirty_workspace_and_graph_replays(dsa):
+    """One workspace, filled with arbitrary bytes up front, serves several
+    calls with different inputs and a captured graph replayed several times:
+    the per-sequence arrival counters must need no clearing, and every result
+    must match the oracle."""
+    import torch
+    topk = 512
+    lens_a = [40000, 17000, 33000, 512, 20001]
+    lens_b = [1000, 39999, 40000, 26000, 600]
+    ia = _small_inputs(5, 40000, 64, 128, lens_a, seed=21)
+    ib = _small_inputs(5, 40000, 64, 128, lens_b, seed=22)
+    n = dsa.dsa_indexer_topk_decode_workspace(5, 40000, 64, 128, topk)
+    for fill in (0xFF, 0x00, 0x5A):
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+        for inp in (ia, ib, ia):
+            note(f"decode dirty workspace fill={fill:#x} lens={inp['lens'].tolist()}")
+            out = dsa.dsa_indexer_topk_decode(dev(inp["q"]), dev(inp["w"]), dev(inp["cache"]), dev(inp["k_scale"]),
+                                              dev(inp["lens"]), topk, want_scores=True, workspace=ws)
+            torch.cuda.synchronize()
+            _compare(host(out[0]), host(out[1]), inp, topk)
+    # graph: capture one call, replay it with eager calls on other inputs in between
+    d = {k: dev(v) for k, v in ia.items()}
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    oi = torch.empty((5, topk), dtype=torch.int32, device="cuda")
+    osc = torch.empty((5, topk), dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on the capture stream
+        dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk, out_idx=oi,
+                                    out_topk_score=osc, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk, out_idx=oi,
+                                    out_topk_score=osc, workspace=ws)
+    for rep in range(3):
+        note(f"decode graph replay {rep}")
+        oi.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        _compare(host(oi), host(osc), ia, topk)
+        eb = dsa.dsa_indexer_topk_decode(dev(ib["q"]), dev(ib["w"]), dev(ib["cache"]), dev(ib["k_scale"]),
+                                         dev(ib["lens"]), topk, want_scores=True, workspace=ws)
+        torch.cuda.synchronize()
+        _compare(host(eb[0]), host(eb[1]), ib, topk)
