@@ -65,8 +65,15 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   constexpr int MB = (H + 31) / 32;
   constexpr int KS = D / 16;              // bf16 MFMA steps along D
   constexpr int HALF = D / 2;             // fp8 bytes of one key half
-  constexpr int NLD = HALF / 16;          // 16-byte loads per lane per key
+  constexpr int NLD = HALF / 16;          // 16-byte loads per lane per 32-key step
+  constexpr int CPR = D / 16;             // 16-byte chunks per key row
+  constexpr int RPB = 256 / D;            // key rows per 256-byte bank sweep
+  static_assert(32 * D == 1024 * NLD, "a step is NLD whole 1 KB loads");
   __shared__ uint32_t hist[HBINS];
+  // per-wave transpose of one 32-key step: row r (a key), chunk c stored at
+  // chunk position c ^ swz(r), swz(r) = (r / RPB) % CPR, so both the
+  // row-contiguous writes and the per-key operand reads are conflict-free
+  __shared__ __attribute__((aligned(16))) uint8_t ktr[DS_NT / 64][32 * D];
   // scores of the workgroup's keys; written out with 16-byte stores after the
   // loop so that no global store is in flight next to the MFMAs and loads
   __shared__ __attribute__((aligned(16))) float sc_stage[DS_KPB];
@@ -120,19 +127,26 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       const int head = 32 * mb + 8 * (j >> 2) + 4 * kh + (j & 3);
       wr[mb][j] = head < H ? bf16_to_f32(p.w[(size_t)b * H + head]) : 0.f;
     }
-  // cache prefetch ring: step u lives in slot u % DS_PF.  Loads are
-  // unconditional: a key past the end of the sequence reads the last key
-  // instead (its score is never stored), so no branch merges values into the
-  // ring registers and no wait is forced on a load still in flight.
+  // cache prefetch ring: step u lives in slot u % DS_PF.  Load i of a step
+  // reads bytes [1024 i, 1024 i + 1024) of its 32 keys, 16 per lane (whole
+  // keys, fully coalesced).  Loads are unconditional: a key past the end of
+  // the sequence reads the last key instead (its score is never stored), so
+  // no branch merges values into the ring registers and no wait is forced on
+  // a load still in flight.
   v4i raw[DS_PF][NLD];
   float kss[DS_PF];
   auto fetch = [&](int slot, int s0) {
-    const int s = min(s0 + col, len - 1);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i)
-      raw[slot][i] = *reinterpret_cast<const v4i*>(cache_b + (size_t)s * D + kh * HALF + 16 * i);
-    kss[slot] = ks_b[s];
+    for (int i = 0; i < NLD; ++i) {
+      const int byte = 1024 * i + 16 * lane;
+      const int r = byte / D;
+      raw[slot][i] = *reinterpret_cast<const v4i*>(cache_b + (size_t)min(s0 + r, len - 1) * D + byte % D);
+    }
+    kss[slot] = ks_b[min(s0 + col, len - 1)];
   };
+  uint8_t* tr = ktr[wave];
+  // this lane's operand chunks: key `col`, chunks kh*NLD + i of its row
+  const int rswz = (col / RPB) % CPR;
 #pragma unroll
   for (int u = 0; u < DS_PF; ++u) fetch(u, chunk_key(u));
 
@@ -148,11 +162,21 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       const int sub = g + u;
       const int s0 = chunk_key(sub);
       {
-        v4i cur[NLD];
+        // through the wave's LDS transpose into per-key operand order
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) cur[i] = raw[u][i];
+        for (int i = 0; i < NLD; ++i) {
+          const int byte = 1024 * i + 16 * lane;
+          const int r = byte / D, c = (byte % D) / 16;
+          *reinterpret_cast<v4i*>(tr + r * D + 16 * (c ^ ((r / RPB) % CPR))) = raw[u][i];
+        }
         const float cks = kss[u];
         fetch(u, chunk_key(min(sub + DS_PF, nstep - 1)));   // past the end: harmless reload
+        wave_lds_sync();
+        v4i cur[NLD];
+#pragma unroll
+        for (int i = 0; i < NLD; ++i)
+          cur[i] = *reinterpret_cast<const v4i*>(tr + col * D + 16 * ((kh * NLD + i) ^ rswz));
+        wave_lds_sync();   // every lane has read before the next step overwrites
 
         // widen 16 fp8 of a load into two 8-element bf16 operands
         v8bf bop[KS];
