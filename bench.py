@@ -45,12 +45,19 @@ def decode_bytes(lens, H, D, topk, B):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank lines removed, so a
+    counter summary stays attached to the code it was taken on."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_attention_token_02_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode())
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(f.encode())
+        h.update(text.encode())
     return h.hexdigest()[:16]
 
 
@@ -297,8 +304,8 @@ def run_fs(args, g, dsa, gen, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="main")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)

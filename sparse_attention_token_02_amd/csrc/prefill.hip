@@ -20,8 +20,10 @@
 //   fp8 path: v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3, unit block
 //   scales); bf16 path: v_mfma_f32_32x32x16_bf16.  Products are exact, the
 //   accumulation is fp32.
-// * Keys are staged through LDS in tiles of 128, double buffered; every wave
-//   reuses each tile for its own queries.  Query operands and the folded head
+// * Keys are staged through LDS in tiles of 256 keys (128 when a key row is
+//   wider than 128 bytes or H <= 16), double buffered, with direct
+//   global-to-LDS loads into swizzled rows; every wave reuses each tile for
+//   its own queries.  Query operands and the folded head
 //   weights w*q_scale stay in registers for the whole work item.  Inside a
 //   tile the MFMAs of one head block overlap the VALU epilogue of the
 //   previous one (two accumulators, explicit issue groups).
