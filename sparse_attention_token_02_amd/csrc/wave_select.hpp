@@ -64,20 +64,25 @@ __device__ __forceinline__ int wave_boundary_digit(const uint32_t* hist, uint32_
   return __builtin_amdgcn_readlane(dig, src);
 }
 
-// Calls body(key) for key_of(i), i < n, over this lane's entries (i = lane
-// + 64 j).  Keys are fetched eight at a time (indices clamped into range, so
-// the loads are unconditional) before any is used, which keeps eight memory
-// reads in flight per lane.
-template <class KeyOf, class Body>
-__device__ __forceinline__ void wave_for_keys(KeyOf key_of, int n, Body body) {
+// Calls body(key) for the keys ordered_key(vals[i]), i < n, in no
+// particular order.  vals is 16-byte aligned; a lane reads four consecutive
+// entries per 16-byte load and issues eight loads (2048 entries per wave)
+// before it uses any.  The float4 holding entry n - 1 is the last one read,
+// so reads stay inside the 16-byte-rounded array.
+template <class Body>
+__device__ __forceinline__ void wave_for_score_keys(const float* vals, int n, Body body) {
   constexpr int U = 8;
-  for (int base = __lane_id(); base < n; base += 64 * U) {
-    uint32_t kk[U];
+  const int nq = (n + 3) >> 2;
+  for (int q0 = __lane_id(); q0 < nq; q0 += 64 * U) {
+    v4f v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) kk[u] = key_of(min(base + 64 * u, n - 1));
+    for (int u = 0; u < U; ++u) v[u] = reinterpret_cast<const v4f*>(vals)[min(q0 + 64 * u, nq - 1)];
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (base + 64 * u < n) body(kk[u]);
+      if (q0 + 64 * u < nq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * (q0 + 64 * u) + e < n) body(ordered_key(v[u][e]));
   }
 }
 
@@ -88,15 +93,14 @@ struct WaveCut {
   uint32_t mask, prefix, take_eq, kth;
 };
 
-// Radix search for the cut that keeps exactly k of the n keys key_of(i),
-// i < n (requires n > k >= 1).  Stops as soon as the boundary bin is kept
-// whole; the k-th key is then the smallest key of that bin (one more pass).
+// Radix search for the cut that keeps exactly k of the n keys of vals[0..n)
+// (requires n > k >= 1).  Stops as soon as the boundary bin is kept whole;
+// the k-th key is then the smallest key of that bin (one more pass).
 // `hist` is 256 words of this wave's LDS.
-template <class KeyOf>
-__device__ WaveCut wave_find_cut(KeyOf key_of, int n, int k, uint32_t* hist) {
+__device__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist) {
   const int lane = __lane_id();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  wave_for_keys(key_of, n, [&](uint32_t key) {
+  wave_for_score_keys(vals, n, [&](uint32_t key) {
     lo = min(lo, key);
     hi = max(hi, key);
   });
@@ -117,7 +121,7 @@ __device__ WaveCut wave_find_cut(KeyOf key_of, int n, int k, uint32_t* hist) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
     wave_lds_sync();
-    wave_for_keys(key_of, n, [&](uint32_t key) {
+    wave_for_score_keys(vals, n, [&](uint32_t key) {
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dm], 1u);
     });
     wave_lds_sync();
@@ -137,7 +141,7 @@ __device__ WaveCut wave_find_cut(KeyOf key_of, int n, int k, uint32_t* hist) {
   if (whole_bin) {
     // the k-th key is the smallest key of the boundary bin
     uint32_t m = 0xFFFFFFFFu;
-    wave_for_keys(key_of, n, [&](uint32_t key) {
+    wave_for_score_keys(vals, n, [&](uint32_t key) {
       if ((key & pmask) == prefix) m = min(m, key);
     });
     kth = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(m));
@@ -145,62 +149,80 @@ __device__ WaveCut wave_find_cut(KeyOf key_of, int n, int k, uint32_t* hist) {
   return WaveCut{pmask, prefix, need, kth};
 }
 
-// k-th largest key (1 <= kp <= n) among the n floats vals[0..n).
+// k-th largest key (1 <= kp <= n) among the n floats vals[0..n) (16-byte aligned).
 __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int kp, uint32_t* hist) {
   if (n == 1) return ordered_key(vals[0]);
   if (kp >= n) {
     uint32_t lo = 0xFFFFFFFFu;
-    for (int e = __lane_id(); e < n; e += 64) lo = min(lo, ordered_key(vals[e]));
+    wave_for_score_keys(vals, n, [&](uint32_t key) { lo = min(lo, key); });
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(lo));
   }
-  return wave_find_cut([&](int e) { return ordered_key(vals[e]); }, n, kp, hist).kth;
+  return wave_find_cut(vals, n, kp, hist).kth;
 }
 
 // Exact top-k of the candidate list (sc[i], ix[i]), i < n, held in global
-// memory in ascending key-index order.  Keeps the k largest scores, ties to
-// the earliest entries, and writes the kept entries in list order to
-// dix[0..) and dsc[0..) (dsc may be null; dix/dsc may alias ix/sc, since an
-// entry never moves to a later position).  Then pads dix with -1 and dsc with
-// -inf up to pad_to.  Returns the number kept, min(n, k).  *tau (if not null)
-// receives the k-th largest score (-inf when n <= k).
+// memory in ascending key-index order (both arrays 16-byte aligned).  Keeps
+// the k largest scores, ties to the earliest entries, and writes the kept
+// entries in list order to dix[0..) and dsc[0..) (dsc may be null; dix/dsc
+// may alias ix/sc: a batch is read whole before any of it is written, and
+// writes never pass the start of the next batch).  Then pads dix with -1 and
+// dsc with -inf up to pad_to.  Returns the number kept, min(n, k).  *tau (if
+// not null) receives the k-th largest score (-inf when n <= k).
 // The caller makes the list's earlier global writes visible first.
 __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
                            uint32_t* hist, float* tau) {
   const int lane = __lane_id();
   WaveCut cut{0u, 0u, 0xFFFFFFFFu, 0u};   // keeps everything
-  if (n > k) cut = wave_find_cut([&](int e) { return ordered_key(sc[e]); }, n, k, hist);
+  if (n > k) cut = wave_find_cut(sc, n, k, hist);
   if (tau) *tau = n > k ? key_to_float(cut.kth) : -__builtin_inff();
   int out = 0;
   uint32_t eq_seen = 0;
-  constexpr int U = 8;
-  for (int base = 0; base < n; base += 64 * U) {
-    // fetch eight groups of 64 entries, then emit them group by group in
-    // list order (a group only writes below its own positions, so the
-    // in-place case never overwrites an entry that is still to be read)
-    float sv[U];
-    int iv[U];
+  constexpr int U = 4;                    // float4 groups per lane and batch
+  const int nq = (n + 3) >> 2;
+  for (int q0 = 0; q0 < nq; q0 += 64 * U) {
+    // the batch: entries 4 (q0 + 64 u + lane) + e, read whole before any write
+    v4f sv[U];
+    v4i iv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = min(base + 64 * u + lane, n - 1);
-      sv[u] = sc[e];
-      iv[u] = ix[e];
+      const int q = min(q0 + 64 * u + lane, nq - 1);
+      sv[u] = reinterpret_cast<const v4f*>(sc)[q];
+      iv[u] = reinterpret_cast<const v4i*>(ix)[q];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool valid = base + 64 * u + lane < n;
-      const uint32_t km = ordered_key(sv[u]) & cut.mask;
-      const bool gt = valid && km > cut.prefix;
-      const bool eq = valid && km == cut.prefix;
-      const uint64_t meq = ballot64(eq);
-      const bool take = gt || (eq && eq_seen + (uint32_t)lanes_below(meq) < cut.take_eq);
-      const uint64_t mt = ballot64(take);
-      if (take) {
-        const int pos = out + lanes_below(mt);
-        dix[pos] = iv[u];
-        if (dsc) dsc[pos] = sv[u];
+      const int e0 = 4 * (q0 + 64 * u + lane);
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool valid = e0 + e < n;
+        const uint32_t km = ordered_key(sv[u][e]) & cut.mask;
+        gt |= (uint32_t)(valid && km > cut.prefix) << e;
+        eq |= (uint32_t)(valid && km == cut.prefix) << e;
       }
-      out += __popcll(mt);
-      eq_seen += (uint32_t)__popcll(meq);
+      // ties are taken in list order: rank = ties before this lane + within it
+      const int neq = __popc(eq);
+      const int eq_incl = wave_incl_sum(neq);
+      uint32_t rank = eq_seen + (uint32_t)(eq_incl - neq);
+      uint32_t take = gt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((eq >> e) & 1u) {
+          if (rank < cut.take_eq) take |= 1u << e;
+          ++rank;
+        }
+      const int nt = __popc(take);
+      const int nt_incl = wave_incl_sum(nt);
+      int pos = out + nt_incl - nt;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((take >> e) & 1u) {
+          dix[pos] = iv[u][e];
+          if (dsc) dsc[pos] = sv[u][e];
+          ++pos;
+        }
+      out += __builtin_amdgcn_readlane(nt_incl, 63);
+      eq_seen += (uint32_t)__builtin_amdgcn_readlane(eq_incl, 63);
     }
   }
   for (int e = out + lane; e < pad_to; e += 64) {
