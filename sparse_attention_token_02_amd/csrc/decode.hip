@@ -33,7 +33,10 @@ namespace {
 
 constexpr int DS_NT = 256;          // score kernel threads
 constexpr int DS_NSUB = 64;         // 32-key steps per wave
-constexpr int DS_PF = 4;            // steps in flight per wave
+#ifndef DS_PF_STEPS
+#define DS_PF_STEPS 4
+#endif
+constexpr int DS_PF = DS_PF_STEPS;  // steps in flight per wave
 constexpr int DS_KPB = (DS_NT / 64) * DS_NSUB * 32;   // keys per workgroup
 constexpr int DS_MAXWG = 32;        // score workgroups per sequence at most (Lmax <= 262144)
 constexpr int HBINS = 4096;         // fine bins: top 12 bits of the order-preserving key
@@ -178,25 +181,19 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
           cur[i] = *reinterpret_cast<const v4i*>(tr + col * D + 16 * ((kh * NLD + i) ^ rswz));
         wave_lds_sync();   // every lane has read before the next step overwrites
 
-        // widen 16 fp8 of a load into two 8-element bf16 operands
-        v8bf bop[KS];
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const uint32_t d0 = (uint32_t)cur[i][2 * h2];
-            const uint32_t d1 = (uint32_t)cur[i][2 * h2 + 1];
-            v4i o = v4i{(int)cvt2<false>(d0), (int)cvt2<true>(d0), (int)cvt2<false>(d1), (int)cvt2<true>(d1)};
-            bop[2 * i + h2] = __builtin_bit_cast(v8bf, o);
-          }
-        }
         v16f acc[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb] = v16f{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+          // widen 8 fp8 (half of a 16-byte load) into one bf16 operand, just in time
+          const uint32_t d0 = (uint32_t)cur[ks >> 1][2 * (ks & 1)];
+          const uint32_t d1 = (uint32_t)cur[ks >> 1][2 * (ks & 1) + 1];
+          const v8bf bop = __builtin_bit_cast(v8bf, v4i{(int)cvt2<false>(d0), (int)cvt2<true>(d0),
+                                                        (int)cvt2<false>(d1), (int)cvt2<true>(d1)});
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_bf16(qa[mb][ks], bop[ks], acc[mb]);
+          for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_bf16(qa[mb][ks], bop, acc[mb]);
+        }
         float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)

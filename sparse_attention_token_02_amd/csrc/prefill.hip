@@ -91,17 +91,20 @@ struct PfCfg {
   static __device__ __forceinline__ int slot_of(int j) { return SPLIT ? 0 : j / HB; }
 };
 
+// The key tiles and the candidate stage come last, so that together with the
+// dynamic sample area that follows the static block they form one span of
+// LDS that the end-of-item selection reuses as per-wave scratch.
 template <int DT, int H, int D>
 struct PfShared {
   using C = PfCfg<DT, H, D>;
-  __attribute__((aligned(1024))) uint8_t ktile[2][C::TK * C::ROWB];   // double-buffered key tile (swizzled)
   __attribute__((aligned(16))) float kscale[2][C::TK];
-  float stage_sc[C::RW][C::TK];            // this tile's accepted candidates, per row
-  int stage_ix[C::RW][C::TK];
   uint32_t whist[WAVES][256];              // per-wave radix histogram (selection, sample quantile)
   __attribute__((aligned(16))) float weff[C::RW * H];   // folded head weights w*q_scale of the item's rows
   int row_cnt[C::RW];
   int item;
+  __attribute__((aligned(1024))) uint8_t ktile[2][C::TK * C::ROWB];   // double-buffered key tile (swizzled)
+  __attribute__((aligned(16))) float stage_sc[C::RW][C::TK];          // this tile's accepted candidates, per row
+  int stage_ix[C::RW][C::TK];
 };
 
 template <bool FP8> struct Opnd;
@@ -563,7 +566,17 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         continue;               // recompute the item without the sample threshold
       }
 
-      // ---- final selection: each wave writes its own rows, in ascending key order
+      // ---- final selection: each wave writes its own rows, in ascending key
+      // order.  The key tiles, the stage and (when it directly follows the
+      // static block) the sample area are free now: each wave gets an equal,
+      // 16-byte aligned share as scratch for its row's scores.
+      uint8_t* scr = &sh.ktile[0][0];
+      const uint8_t* scr_static_end = reinterpret_cast<const uint8_t*>(&sh.stage_ix[0][0]) + sizeof(sh.stage_ix);
+      size_t scr_bytes = (size_t)(scr_static_end - scr);
+      if (reinterpret_cast<const uint8_t*>(dyn_lds) == scr_static_end)
+        scr_bytes += (size_t)C::RW * p.sample_m * sizeof(float);
+      const int lcap = (int)(scr_bytes / WAVES / 16) * 4;   // floats per wave, a multiple of 4
+      float* lbuf = reinterpret_cast<float*>(scr) + (size_t)wave * lcap;
 #pragma unroll 1
       for (int rr = 0; rr < C::QPW; ++rr) {
         const int row = wave * C::QPW + rr;
@@ -572,7 +585,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         int* dix = p.out_idx + (size_t)t * p.topk;
         float* dsc = p.out_score ? p.out_score + (size_t)t * p.topk : nullptr;
         wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix, p.topk,
-                    sh.whist[wave], nullptr);
+                    sh.whist[wave], nullptr, lbuf, lcap);
       }
       break;
     }

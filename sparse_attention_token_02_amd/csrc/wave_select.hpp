@@ -95,15 +95,23 @@ struct WaveCut {
 
 // Radix search for the cut that keeps exactly k of the n keys of vals[0..n)
 // (requires n > k >= 1).  Stops as soon as the boundary bin is kept whole;
-// the k-th key is then the smallest key of that bin (one more pass).
-// `hist` is 256 words of this wave's LDS.
-__device__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist) {
+// the k-th key is then the smallest key of that bin, found with one more
+// pass when need_kth (else kth is left 0).  `hist` is 256 words of this
+// wave's LDS.  lo_hi, when given, holds the smallest and largest key
+// (reduced over the wave), which saves the first pass.
+__device__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist, bool need_kth = true,
+                                 const uint32_t* lo_hi = nullptr) {
   const int lane = __lane_id();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  wave_for_score_keys(vals, n, [&](uint32_t key) {
-    lo = min(lo, key);
-    hi = max(hi, key);
-  });
+  if (lo_hi) {
+    lo = lo_hi[0];
+    hi = lo_hi[1];
+  } else {
+    wave_for_score_keys(vals, n, [&](uint32_t key) {
+      lo = min(lo, key);
+      hi = max(hi, key);
+    });
+  }
   // Every lane holds the same reduced values; readfirstlane makes that
   // visible to the compiler so the radix loop below is scalar control flow.
   lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(lo));
@@ -138,7 +146,8 @@ __device__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist
     }
   }
   uint32_t kth = prefix;   // exact when every bit was resolved
-  if (whole_bin) {
+  if (whole_bin && !need_kth) kth = 0u;
+  if (whole_bin && need_kth) {
     // the k-th key is the smallest key of the boundary bin
     uint32_t m = 0xFFFFFFFFu;
     wave_for_score_keys(vals, n, [&](uint32_t key) {
@@ -169,11 +178,47 @@ __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int k
 // dsc with -inf up to pad_to.  Returns the number kept, min(n, k).  *tau (if
 // not null) receives the k-th largest score (-inf when n <= k).
 // The caller makes the list's earlier global writes visible first.
+// lbuf (16-byte aligned wave-private LDS of lcap floats, lcap a multiple of
+// 4, or null): when the list fits, its scores are copied there once and every
+// later pass reads them from LDS (then dsc must not alias sc).
 __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
-                           uint32_t* hist, float* tau) {
+                           uint32_t* hist, float* tau, float* lbuf = nullptr, int lcap = 0) {
   const int lane = __lane_id();
   WaveCut cut{0u, 0u, 0xFFFFFFFFu, 0u};   // keeps everything
-  if (n > k) cut = wave_find_cut(sc, n, k, hist);
+  const float* ksc = sc;                  // where the scores are read from
+  uint32_t lo_hi[2];
+  bool have_lo_hi = false;
+  if (lbuf && n > k && n <= lcap) {
+    // copy the scores, rounded up to whole float4 groups (inside the list's
+    // 16-byte-rounded storage and inside lcap), eight loads in flight per
+    // lane, and take the smallest and largest key on the way
+    constexpr int UC = 8;
+    const int nq = (n + 3) >> 2;
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int q0 = lane; q0 < nq; q0 += 64 * UC) {
+      v4f v[UC];
+#pragma unroll
+      for (int u = 0; u < UC; ++u) v[u] = reinterpret_cast<const v4f*>(sc)[min(q0 + 64 * u, nq - 1)];
+#pragma unroll
+      for (int u = 0; u < UC; ++u)
+        if (q0 + 64 * u < nq) {
+          reinterpret_cast<v4f*>(lbuf)[q0 + 64 * u] = v[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * (q0 + 64 * u) + e < n) {
+              const uint32_t key = ordered_key(v[u][e]);
+              lo = min(lo, key);
+              hi = max(hi, key);
+            }
+        }
+    }
+    lo_hi[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_min_u32(lo));
+    lo_hi[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_u32(hi));
+    have_lo_hi = true;
+    wave_lds_sync();
+    ksc = lbuf;
+  }
+  if (n > k) cut = wave_find_cut(ksc, n, k, hist, tau != nullptr, have_lo_hi ? lo_hi : nullptr);
   if (tau) *tau = n > k ? key_to_float(cut.kth) : -__builtin_inff();
   int out = 0;
   uint32_t eq_seen = 0;
@@ -186,7 +231,7 @@ __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = min(q0 + 64 * u + lane, nq - 1);
-      sv[u] = reinterpret_cast<const v4f*>(sc)[q];
+      sv[u] = reinterpret_cast<const v4f*>(ksc)[q];
       iv[u] = reinterpret_cast<const v4i*>(ix)[q];
     }
 #pragma unroll
@@ -200,9 +245,13 @@ __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* 
         gt |= (uint32_t)(valid && km > cut.prefix) << e;
         eq |= (uint32_t)(valid && km == cut.prefix) << e;
       }
-      // ties are taken in list order: rank = ties before this lane + within it
+      // ties are taken in list order: rank = ties before this lane + within
+      // it.  One scan carries both counts: ties in the low 16 bits, kept
+      // entries above the cut in the high 16 (each at most 256 per wave)
       const int neq = __popc(eq);
-      const int eq_incl = wave_incl_sum(neq);
+      const int ngt = __popc(gt);
+      const int both_incl = wave_incl_sum(neq | (ngt << 16));
+      const int eq_incl = both_incl & 0xFFFF;
       uint32_t rank = eq_seen + (uint32_t)(eq_incl - neq);
       uint32_t take = gt;
 #pragma unroll
@@ -211,9 +260,15 @@ __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* 
           if (rank < cut.take_eq) take |= 1u << e;
           ++rank;
         }
-      const int nt = __popc(take);
-      const int nt_incl = wave_incl_sum(nt);
-      int pos = out + nt_incl - nt;
+      // kept ties of this lane and of the lanes before it: the ties before
+      // this lane that are still below take_eq, plus this lane's own
+      const int eq_before = eq_incl - neq;
+      const uint32_t room_u = cut.take_eq > eq_seen ? cut.take_eq - eq_seen : 0u;   // ties still to take
+      const int room = (int)min(room_u, 0x7FFFFFFFu);
+      const int teq_before = min(eq_before, room);
+      const int teq_incl = min(eq_incl, room);
+      const int nt_incl = (both_incl >> 16) + teq_incl;
+      int pos = out + (both_incl >> 16) - ngt + teq_before;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((take >> e) & 1u) {
