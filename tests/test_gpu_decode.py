@@ -156,3 +156,11 @@ def test_decode_reused_dirty_workspace_and_graph_replays(dsa):
                                          dev(ib["lens"]), topk, want_scores=True, workspace=ws)
         torch.cuda.synchronize()
         _compare(host(eb[0]), host(eb[1]), ib, topk)
+
+
+def test_decode_topk_one(dsa):
+    lens = [3000, 1, 2, 1777]
+    inp = _small_inputs(4, 3000, 64, 128, lens, seed=31)
+    note("decode topk=1")
+    idx, sc = _run(dsa, inp, 1)
+    _compare(idx, sc, inp, 1)

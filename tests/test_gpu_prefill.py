@@ -166,3 +166,36 @@ def test_prefill_32k_full_size_sampled_rows(dsa):
     res = oracle.prefill(host_inp["q"], host_inp["q_scale"], host_inp["k"], host_inp["k_scale"], host_inp["w"],
                          "fp8", topk, rows=rows, return_scores=True)
     _compare(idx_h, sc_h, res, rows, topk)
+
+
+# Every (dtype, H, D) the library builds: the H >= 32 split-head layout, the
+# H = 16 and H = 8 layouts (one and two queries per lane half), and both tile
+# sizes.  Ragged L (not a multiple of the 8- to 32-row work item or of a tile).
+BUILT = [("fp8", 64, 128), ("fp8", 64, 64), ("fp8", 32, 128), ("fp8", 32, 64), ("fp8", 16, 128),
+         ("fp8", 16, 64), ("fp8", 8, 128), ("fp8", 8, 64), ("bf16", 64, 64), ("bf16", 32, 128),
+         ("bf16", 32, 64), ("bf16", 16, 128), ("bf16", 16, 64), ("bf16", 8, 128), ("bf16", 8, 64)]
+
+
+@pytest.mark.parametrize("dt,H,D", BUILT)
+def test_every_built_configuration(dsa, dt, H, D):
+    L, topk = 1109, 96
+    cfg = dict(kind="prefill", L=L, H=H, D=D, topk=topk, dtype=dt, seed=H + D + (dt == "bf16"),
+               heavy_count=11, heavy_factor=3.0, qk_div=8.0, w_div=8.0)
+    note(f"prefill configuration {dt} H={H} D={D} L={L} k={topk}")
+    inp = gen.prefill_inputs(cfg)
+    idx, sc, _ = _run(dsa, inp, cfg, want_scores=True)
+    check_structure_all(idx, topk)
+    rows = sample_rows(L, topk, 48, seed=H * D)
+    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
+
+
+@pytest.mark.parametrize("L,topk", [(700, 1), (5003, 4096)])
+def test_topk_limits(dsa, L, topk):
+    """The smallest k and the largest the library accepts."""
+    cfg = dict(gen.CONFIGS["prefill_32k"], L=L, topk=topk, heavy_count=L // 100)
+    note(f"prefill topk limit L={L} k={topk}")
+    inp = gen.prefill_inputs(cfg)
+    idx, sc, _ = _run(dsa, inp, cfg, want_scores=True)
+    check_structure_all(idx, topk)
+    rows = sample_rows(L, topk, 24, seed=topk)
+    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
