@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     // 64g + i of the tile.  Keys past the end read the last key (always
     // masked), so every load is unconditional.  Completion is awaited (vmcnt)
     // right before the barrier that publishes the tile.
-    auto issue_tile = [&](int kt, int buf) {
+    auto issue_tile = [&](int kt, uint8_t* tdst, float* kdst) {
 #pragma unroll
       for (int i = 0; i < C::NLD / WAVES; ++i) {
         const int g = wave + WAVES * i;
@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int c = (pos % C::CPR) ^ ((r / C::RPB) & (C::CPR - 1));
         const uint8_t* src = p.k + (size_t)min(kt + r, L - 1) * C::ROWB + c * 16;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)&sh.ktile[buf][1024 * g], 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(tdst + 1024 * g), 16, 0, 0);
       }
       if (wave < C::TK / 64) {
         // H >= 32 reads k_scale lane-major: key 64*pair + lane at lane*(TK/64) + pair
@@ -245,9 +245,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int kk = C::SPLIT ? 64 * (pos % (C::TK / 64)) + pos / (C::TK / 64) : pos;
         if (p.k_scale) {
           __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(p.k_scale + min(kt + kk, L - 1)),
-                                           (__attribute__((address_space(3))) void*)&sh.kscale[buf][64 * wave], 4, 0, 0);
+                                           (__attribute__((address_space(3))) void*)(kdst + 64 * wave), 4, 0, 0);
         } else {
-          sh.kscale[buf][pos] = 1.f;
+          kdst[pos] = 1.f;
         }
       }
     };
@@ -270,8 +270,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     //   H >= 32: on_score(pair, score) per subtile pair; the halves trade
     //            partial head sums so that lane l holds the full score of key
     //            64*pair + l (half 0 finishes the even subtile, half 1 the odd).
-    auto tile_scores = [&](int buf, auto&& on_score) {
-      const uint8_t* bp = &sh.ktile[buf][col * C::ROWB];
+    auto tile_scores = [&](const uint8_t* tile, const float* ksc_t, auto&& on_score) {
+      const uint8_t* bp = tile + col * C::ROWB;
       auto load_b = [&](int sub, int ks) -> OT {
         const uint8_t* rp = bp + 32 * sub * C::ROWB;
         if constexpr (C::FP8) {
@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       // (stored lane-major, one vector read)
       float ksc_v[C::TK / 64];
       if constexpr (C::SPLIT) {
-        const float* kp = &sh.kscale[buf][lane * (C::TK / 64)];
+        const float* kp = ksc_t + lane * (C::TK / 64);
         if constexpr (C::TK == 256) {
           const float4 v = *reinterpret_cast<const float4*>(kp);
           ksc_v[0] = v.x; ksc_v[1] = v.y; ksc_v[2] = v.z; ksc_v[3] = v.w;
@@ -342,7 +342,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
             pend_id = sub >> 1;
           }
         } else {
-          const float ksc = sh.kscale[buf][32 * sub + col];
+          const float ksc = ksc_t[32 * sub + col];
 #pragma unroll
           for (int r = 0; r < C::QPH; ++r)
             pend_sc[r] = ((part[r][0] + part[r][1]) + (part[r][2] + part[r][3])) * ksc;
@@ -419,7 +419,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         tau[r] = -__builtin_inff();
       }
 
-      issue_tile(tile_key(0), 0);
+      issue_tile(tile_key(0), sh.ktile[0], sh.kscale[0]);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
 
@@ -427,7 +427,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int kt = tile_key(it);
         const bool sampling = it < stile;
         const int buf = it & 1;
-        if (it + 1 < total) issue_tile(tile_key(it + 1), buf ^ 1);
+        // The two tile buffers are distinct; saying so (restrict) lets the
+        // compiler read the current tile without first waiting for the load
+        // of the next one into the other buffer.
+        auto tile_body = [&](const uint8_t* __restrict__ tile, const float* __restrict__ ksc_t,
+                             uint8_t* __restrict__ ntile, float* __restrict__ nksc) {
+        if (it + 1 < total) issue_tile(tile_key(it + 1), ntile, nksc);
 
         // The two branches run the same MFMA sequence; the distinct markers
         // keep the compiler from hoisting it into the common predecessor,
@@ -440,9 +445,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         if (sampling) {
           asm volatile("; sample tile" ::: "memory");
           if constexpr (C::SPLIT) {
-            tile_scores(buf, [&](int pair, float sc) { smp_row[it * C::TK + 64 * pair + lane] = sc; });
+            tile_scores(tile, ksc_t, [&](int pair, float sc) { smp_row[it * C::TK + 64 * pair + lane] = sc; });
           } else {
-            tile_scores(buf, [&](int sub, const float (&sc)[C::QPH]) {
+            tile_scores(tile, ksc_t, [&](int sub, const float (&sc)[C::QPH]) {
 #pragma unroll
               for (int r = 0; r < C::QPH; ++r) smp_lane[r * p.sample_m + it * C::TK + 32 * sub] = sc[r];
             });
@@ -455,7 +460,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
           // consecutive words.  Filter: strictly above max(tau, tau0).
           if constexpr (C::SPLIT) {
             const int tr = t0 + wave;
-            tile_scores(buf, [&](int pair, float score) {
+            tile_scores(tile, ksc_t, [&](int pair, float score) {
               const int s = kt + 64 * pair + lane;
               if constexpr (DENSE) {
                 if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)tr * L + s] = s <= tr ? score : -__builtin_inff();
@@ -470,7 +475,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
               scnt[0] += np;
             });
           } else {
-            tile_scores(buf, [&](int sub, const float (&sc)[C::QPH]) {
+            tile_scores(tile, ksc_t, [&](int sub, const float (&sc)[C::QPH]) {
               const int s = kt + 32 * sub + col;
               const uint32_t lt = (1u << col) - 1u;
 #pragma unroll
@@ -493,6 +498,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
             });
           }
         }
+        };
+        tile_body(sh.ktile[buf], sh.kscale[buf], sh.ktile[buf ^ 1], sh.kscale[buf ^ 1]);
 
         if (!sampling) {
           // ---- move this tile's staged candidates to the rows' lists (one
