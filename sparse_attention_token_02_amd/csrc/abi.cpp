@@ -185,7 +185,7 @@ struct DecodeWs {
   int ld;
 };
 
-static DecodeWs decode_ws(int B, int Lmax, int topk) {
+static DecodeWs decode_ws(int B, int Lmax) {
   DecodeWs w{};
   w.ld = (int)align_up((size_t)Lmax, 64);
   size_t off = 0;
@@ -208,7 +208,7 @@ static DecodeWs decode_ws(int B, int Lmax, int topk) {
   return w;
 }
 
-static size_t decode_ws_bytes(int B, int Lmax, int topk) { return decode_ws(B, Lmax, topk).total; }
+static size_t decode_ws_bytes(int B, int Lmax) { return decode_ws(B, Lmax).total; }
 
 dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int topk, size_t* bytes) {
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
@@ -216,7 +216,7 @@ dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int 
     return fail(DSA_ERR_INVALID_ARG, "bad decode sizes B=%d Lmax=%d H=%d D=%d topk=%d", B, Lmax, H, D, topk);
   if (Lmax > kMaxDecodeLmax || !dsa::decode_supported(H, D, Lmax))
     return fail(DSA_ERR_UNSUPPORTED, "decode kernels are not built for H=%d D=%d Lmax=%d", H, D, Lmax);
-  *bytes = decode_ws_bytes(B, Lmax, topk);
+  *bytes = decode_ws_bytes(B, Lmax);
   return ok();
 }
 
@@ -245,7 +245,7 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
   p.out_idx = out_idx;
   p.out_score = out_topk_score;
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  const DecodeWs lay = decode_ws(B, Lmax, topk);
+  const DecodeWs lay = decode_ws(B, Lmax);
   p.ld = lay.ld;
   p.scores = reinterpret_cast<float*>(base + lay.scores);
   p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
