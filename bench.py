@@ -11,7 +11,7 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|fs_47``) print their own line.
+(``--workload tiny|prefill_196k|fs_47|fs_decode_47``) print their own line.
 """
 from __future__ import annotations
 
@@ -249,6 +249,8 @@ def run_workload(args):
                 "config": {"workload": name, **{k: v for k, v in cfg.items() if k != "kind"}}}
     if name == "fs_47":
         return run_fs(args, g, dsa, gen, stream)
+    if name == "fs_decode_47":
+        return run_fs_decode(args, g, dsa, gen, stream)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -292,6 +294,55 @@ def run_fs(args, g, dsa, gen, stream):
     res["overlap_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
     res["overlap_adjacent_mean"] = round(float(sum(ratio[i, i + 1] for i in range(N - 1)) / (N - 1)), 4)
     res["overlap_matrix"] = [[round(float(x), 4) for x in row] for row in ratio]
+    for pname, pat in gen.FS_PATTERNS.items():
+        src = dsa.indexcache_resolve(pat)
+        s_layers = [l for l in range(N) if pat[l] == "S"]
+        if s_layers:
+            res.setdefault("s_layer_mean_overlap_with_source", {})[pname] = round(
+                float(sum(ratio[l, src[l]] for l in s_layers) / len(s_layers)), 4)
+    return res
+
+
+def run_fs_decode(args, g, dsa, gen, stream):
+    """One decode step (32 sequences x 131072 cached tokens) through the
+    layer-reuse schedule over 47 layers, each with its own key cache: indexer
+    time per step for each pattern, and the cross-layer overlap of the all-F
+    selections (rows = sequences)."""
+    import torch
+    cfg = gen.CONFIGS["fs_decode_47"]
+    N, B, Lmax, H, D, topk = cfg["N"], cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"], cfg["topk"]
+    dev = g.device
+    log("generating 47 decode layers")
+    layers = [g.fs_decode_layer_inputs(cfg, l) for l in range(N)]
+    lens = layers[0]["lens"]
+    ws = torch.empty(dsa.dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dtype=torch.uint8, device=dev)
+    tcache = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    pick = lambda key: [layers[l][key] for l in range(N)]
+    times = {}
+    for pname, pat in gen.FS_PATTERNS.items():
+        fn = lambda: dsa.indexcache_run_decode_layers(pat, pick("q"), pick("w"), pick("cache"), pick("k_scale"),
+                                                      lens, topk, tcache=tcache, workspace=ws, stream=stream)
+        ms = time_calls(fn, max(1, args.steps), max(0, args.warmup), stream)
+        times[pname] = sum(ms) / len(ms)
+    nF = {p: pat.count("F") for p, pat in gen.FS_PATTERNS.items()}
+    per_layer = decode_bytes(gen.decode_lens(cfg), H, D, topk, B)
+    gbps = nF["all_F"] * per_layer / (times["all_F"] * 1e-3) / 1e9
+    res = {"metric": METRIC, "workload": "fs_decode_47", "value": round(gbps, 1), "unit": "GB/s",
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+           "config": {"workload": "fs_decode_47", "N": N, "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk},
+           "step_us": {p: round(v * 1e3, 1) for p, v in times.items()},
+           "per_F_layer_us": round(times["all_F"] * 1e3 / N, 2),
+           "indexer_time_saved_frac": {p: round(1 - times[p] / times["all_F"], 4) for p in times},
+           "ideal_saved_frac": {p: round(1 - nF[p] / N, 4) for p in times}}
+    keep = [torch.empty((B, topk), dtype=torch.int32, device=dev) for _ in range(N)]
+    hook = lambda layer, src, tc: keep[layer].copy_(tc)
+    dsa.indexcache_run_decode_layers(gen.FS_PATTERNS["all_F"], pick("q"), pick("w"), pick("cache"),
+                                     pick("k_scale"), lens, topk, tcache=tcache, hook=hook, workspace=ws,
+                                     stream=stream)
+    torch.cuda.synchronize()
+    _, ratio = dsa.topk_overlap_matrix(keep, topk, row_begin=0, row_end=B)
+    res["overlap_adjacent_mean"] = round(float(sum(ratio[i, i + 1] for i in range(N - 1)) / (N - 1)), 4)
     for pname, pat in gen.FS_PATTERNS.items():
         src = dsa.indexcache_resolve(pat)
         s_layers = [l for l in range(N) if pat[l] == "S"]

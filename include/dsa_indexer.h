@@ -168,13 +168,41 @@ dsa_status indexcache_run_layers(const char* pattern, int N,
                                  indexcache_layer_fn hook, void* user,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The same schedule for one decode step ([IS] 2: at decode every layer runs
+ * its indexer at every step; [IC] 4.2: the decode-throughput gain comes from
+ * the S layers skipping it).  An F layer runs dsa_indexer_topk_decode with its
+ * own q, w and key cache into `tcache`; an S layer enqueues nothing and
+ * reuses `tcache` in place.
+ * q, w, k_cache, k_scale: host arrays of N device pointers with the shapes of
+ *            dsa_indexer_topk_decode (entries of S layers are not read and may
+ *            be NULL).
+ * seq_lens   [B] int32, device, shared by every layer (one step of B
+ *            sequences).
+ * tcache     [B, topk] int32, caller-owned, overwritten at every F layer.
+ * src_layer_out host [N] or NULL.  hook may be NULL; it runs after every
+ * layer as in indexcache_run_layers.
+ * The workspace is the decode workspace for (B, Lmax, H, D, topk).  Every F
+ * layer is validated before anything is enqueued.
+ */
+dsa_status indexcache_run_decode_layers(const char* pattern, int N,
+                                        const uint16_t* const* q, const uint16_t* const* w,
+                                        const uint8_t* const* k_cache, const float* const* k_scale,
+                                        const int32_t* seq_lens, int B, int Lmax, int H, int D, int topk,
+                                        int32_t* tcache, int32_t* src_layer_out,
+                                        indexcache_layer_fn hook, void* user,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Cross-layer overlap.  [IC] 1.2.
  * ------------------------------------------------------------------------ */
 
 /*
  * idx        host array of N device pointers, each [L, topk] int32, ascending
- *            non-negative indices then -1 padding (the selection outputs above)
+ *            non-negative indices then -1 padding (the selection outputs above:
+ *            prefill rows, whose keys are <= t, or decode rows, one per
+ *            sequence, whose keys run up to len_b - 1).  Keys above 2^30 - 1
+ *            are not counted.
  * rows       t = row_begin, row_begin + row_stride, ... < row_end
  *            (0 <= row_begin < row_end <= L, row_stride >= 1)
  * out_counts [N, N] uint64, device: C[i][j] = sum over rows of |T_i(t) ∩ T_j(t)|

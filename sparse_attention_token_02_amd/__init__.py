@@ -29,7 +29,7 @@ EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
     "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill",
     "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode",
-    "indexcache_resolve", "indexcache_run_layers", "topk_overlap_matrix",
+    "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers", "topk_overlap_matrix",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -61,6 +61,11 @@ _lib.indexcache_run_layers.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(_vp
                                        ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                        _i32, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(ctypes.c_int32),
                                        HOOK_T, _vp, _vp, _sz, _vp]
+_lib.indexcache_run_decode_layers.restype = _i32
+_lib.indexcache_run_decode_layers.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                              ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _i32, _i32, _i32,
+                                              _i32, _i32, _vp, ctypes.POINTER(ctypes.c_int32), HOOK_T, _vp, _vp,
+                                              _sz, _vp]
 _lib.topk_overlap_matrix.restype = _i32
 _lib.topk_overlap_matrix.argtypes = [ctypes.POINTER(_vp), _i32, _i32, _i32, _i64, _i64, _i64, _vp,
                                      ctypes.POINTER(ctypes.c_double), _vp]
@@ -217,6 +222,41 @@ def indexcache_run_layers(pattern: str, q, q_scale, k, k_scale, w, topk: int, dt
         pattern.encode(), N, _ptr_array(q), _ptr_array(q_scale) if q_scale is not None else None,
         q_scale_head_stride, _ptr_array(k), _ptr_array(k_scale) if k_scale is not None else None,
         _ptr_array(w), L, H, D, topk, _dt(dt), _ptr(tcache), src, cb, None, _ptr(ws), ws.numel(),
+        _stream(stream)))
+    if errors:
+        raise errors[0]
+    return tcache, list(src[:N])
+
+
+def indexcache_run_decode_layers(pattern: str, q, w, k_cache, k_scale, seq_lens, topk: int, *, tcache=None,
+                                 hook=None, workspace=None, stream=None):
+    """One decode step through the F/S schedule.  q, w, k_cache, k_scale are
+    per-layer lists of device tensors with the shapes of
+    ``dsa_indexer_topk_decode`` (entries of S layers may be None); seq_lens
+    [B] int32 is shared by all layers.  ``hook(layer, src_layer, tcache)`` as
+    in ``indexcache_run_layers``.  Returns (tcache [B,topk], src_layer list)."""
+    import torch
+    N = len(pattern)
+    f0 = next(i for i, c in enumerate(pattern) if c == "F") if "F" in pattern else 0
+    B, H, D = q[f0].shape
+    Lmax = k_cache[f0].shape[1]
+    dev = q[f0].device
+    if tcache is None:
+        tcache = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace)
+    src = (ctypes.c_int32 * max(N, 1))()
+    errors = []
+
+    def _hook(layer, src_layer, idx_ptr, stream_ptr, user):
+        try:
+            hook(layer, src_layer, tcache)
+        except Exception as e:  # surfaced after the call returns
+            errors.append(e)
+
+    cb = HOOK_T(_hook) if hook is not None else HOOK_T()
+    _check(_lib.indexcache_run_decode_layers(
+        pattern.encode(), N, _ptr_array(q), _ptr_array(w), _ptr_array(k_cache), _ptr_array(k_scale),
+        _ptr(seq_lens), B, Lmax, H, D, topk, _ptr(tcache), src, cb, None, _ptr(ws), ws.numel(),
         _stream(stream)))
     if errors:
         raise errors[0]

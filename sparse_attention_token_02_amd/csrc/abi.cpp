@@ -144,6 +144,96 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   return DSA_OK;
 }
 
+// Decode workspace: score rows [B, ld] fp32, per-workgroup histograms,
+// selection bitmaps, candidate keys and indices [B, Lmax] each, candidate
+// counts and the per-sequence cut (bin of the k-th score, keys above it).
+struct DecodeWs {
+  size_t scores, hist, bitmap, ckey, cidx, ccnt, cut, total;
+  int ld;
+};
+
+DecodeWs decode_ws(int B, int Lmax) {
+  DecodeWs w{};
+  w.ld = (int)align_up((size_t)Lmax, 64);
+  size_t off = 0;
+  w.scores = off;
+  off += align_up((size_t)B * w.ld * 4, 256);
+  w.hist = off;
+  const dsa::DecodeWsSizes z = dsa::decode_ws_sizes(Lmax);
+  off += align_up((size_t)B * z.hist_words * 4, 256);
+  w.bitmap = off;
+  off += align_up((size_t)B * z.bitmap_words * 4, 256);
+  w.ckey = off;
+  off += align_up((size_t)B * Lmax * 4, 256);
+  w.cidx = off;
+  off += align_up((size_t)B * Lmax * 4, 256);
+  w.ccnt = off;
+  off += align_up((size_t)B * z.cand_cnt * 4, 256);
+  w.cut = off;
+  off += align_up((size_t)B * 8, 256);
+  w.total = off;
+  return w;
+}
+
+size_t decode_ws_bytes(int B, int Lmax) { return decode_ws(B, Lmax).total; }
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* w;
+  const uint8_t* cache;
+  const float* k_scale;
+  const int32_t* lens;
+  int B, Lmax, H, D, topk;
+  int32_t* out_idx;
+  float* out_score;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+dsa_status validate_decode(const DecodeArgs& a) {
+  if (a.B < 1 || a.Lmax < 1 || a.topk < 1 || a.topk > kMaxTopk || a.H < 1 || a.D < 1)
+    return fail(DSA_ERR_INVALID_ARG, "bad decode sizes B=%d Lmax=%d H=%d D=%d topk=%d", a.B, a.Lmax, a.H, a.D,
+                a.topk);
+  if (a.Lmax > kMaxDecodeLmax || !dsa::decode_supported(a.H, a.D, a.Lmax))
+    return fail(DSA_ERR_UNSUPPORTED, "decode kernels are not built for H=%d D=%d Lmax=%d", a.H, a.D, a.Lmax);
+  if (!a.q || !a.w || !a.cache || !a.k_scale || !a.lens || !a.out_idx)
+    return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache, k_scale, seq_lens and out_idx must not be NULL");
+  if (!aligned16(a.q) || !aligned16(a.cache)) return fail(DSA_ERR_INVALID_ARG, "q and k_cache must be 16-byte aligned");
+  const size_t need = decode_ws_bytes(a.B, a.Lmax);
+  if (!a.ws || a.ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, a.ws ? a.ws_bytes : (size_t)0);
+  if (!aligned16(a.ws)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return DSA_OK;
+}
+
+dsa_status launch_decode(const DecodeArgs& a) {
+  dsa::DecodeParams p{};
+  p.q = a.q;
+  p.w = a.w;
+  p.cache = a.cache;
+  p.k_scale = a.k_scale;
+  p.lens = a.lens;
+  p.B = a.B;
+  p.Lmax = a.Lmax;
+  p.topk = a.topk;
+  p.out_idx = a.out_idx;
+  p.out_score = a.out_score;
+  uint8_t* base = static_cast<uint8_t*>(a.ws);
+  const DecodeWs lay = decode_ws(a.B, a.Lmax);
+  p.ld = lay.ld;
+  p.scores = reinterpret_cast<float*>(base + lay.scores);
+  p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
+  p.cand_key = reinterpret_cast<uint32_t*>(base + lay.ckey);
+  p.cand_idx = reinterpret_cast<int*>(base + lay.cidx);
+  p.bitmap = reinterpret_cast<uint32_t*>(base + lay.bitmap);
+  p.cand_cnt = reinterpret_cast<int*>(base + lay.ccnt);
+  p.cut = reinterpret_cast<int2*>(base + lay.cut);
+  hipError_t e = dsa::decode_launch(p, a.H, a.D, a.stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,39 +267,6 @@ dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t
 
 // ---------------------------------------------------------------------------
 
-// Decode workspace: score rows [B, ld] fp32, per-workgroup histograms,
-// selection bitmaps, candidate keys and indices [B, Lmax] each, candidate
-// counts and the per-sequence cut (bin of the k-th score, keys above it).
-struct DecodeWs {
-  size_t scores, hist, bitmap, ckey, cidx, ccnt, cut, total;
-  int ld;
-};
-
-static DecodeWs decode_ws(int B, int Lmax) {
-  DecodeWs w{};
-  w.ld = (int)align_up((size_t)Lmax, 64);
-  size_t off = 0;
-  w.scores = off;
-  off += align_up((size_t)B * w.ld * 4, 256);
-  w.hist = off;
-  const dsa::DecodeWsSizes z = dsa::decode_ws_sizes(Lmax);
-  off += align_up((size_t)B * z.hist_words * 4, 256);
-  w.bitmap = off;
-  off += align_up((size_t)B * z.bitmap_words * 4, 256);
-  w.ckey = off;
-  off += align_up((size_t)B * Lmax * 4, 256);
-  w.cidx = off;
-  off += align_up((size_t)B * Lmax * 4, 256);
-  w.ccnt = off;
-  off += align_up((size_t)B * z.cand_cnt * 4, 256);
-  w.cut = off;
-  off += align_up((size_t)B * 8, 256);
-  w.total = off;
-  return w;
-}
-
-static size_t decode_ws_bytes(int B, int Lmax) { return decode_ws(B, Lmax).total; }
-
 dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int topk, size_t* bytes) {
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
   if (B < 1 || Lmax < 1 || topk < 1 || topk > kMaxTopk || H < 1 || D < 1)
@@ -224,38 +281,12 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
                                    const float* k_scale, const int32_t* seq_lens, int B, int Lmax, int H, int D,
                                    int topk, int32_t* out_idx, float* out_topk_score, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  size_t need = 0;
-  dsa_status st = dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk, &need);
+  DecodeArgs a{q, w, k_cache, k_scale, seq_lens, B, Lmax, H, D, topk, out_idx, out_topk_score, workspace,
+               workspace_bytes, static_cast<hipStream_t>(stream)};
+  dsa_status st = validate_decode(a);
   if (st != DSA_OK) return st;
-  if (!q || !w || !k_cache || !k_scale || !seq_lens || !out_idx)
-    return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache, k_scale, seq_lens and out_idx must not be NULL");
-  if (!aligned16(q) || !aligned16(k_cache)) return fail(DSA_ERR_INVALID_ARG, "q and k_cache must be 16-byte aligned");
-  if (!workspace || workspace_bytes < need)
-    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  dsa::DecodeParams p{};
-  p.q = q;
-  p.w = w;
-  p.cache = k_cache;
-  p.k_scale = k_scale;
-  p.lens = seq_lens;
-  p.B = B;
-  p.Lmax = Lmax;
-  p.topk = topk;
-  p.out_idx = out_idx;
-  p.out_score = out_topk_score;
-  uint8_t* base = static_cast<uint8_t*>(workspace);
-  const DecodeWs lay = decode_ws(B, Lmax);
-  p.ld = lay.ld;
-  p.scores = reinterpret_cast<float*>(base + lay.scores);
-  p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
-  p.cand_key = reinterpret_cast<uint32_t*>(base + lay.ckey);
-  p.cand_idx = reinterpret_cast<int*>(base + lay.cidx);
-  p.bitmap = reinterpret_cast<uint32_t*>(base + lay.bitmap);
-  p.cand_cnt = reinterpret_cast<int*>(base + lay.ccnt);
-  p.cut = reinterpret_cast<int2*>(base + lay.cut);
-  hipError_t e = dsa::decode_launch(p, H, D, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  st = launch_decode(a);
+  if (st != DSA_OK) return st;
   return ok();
 }
 
@@ -306,6 +337,45 @@ dsa_status indexcache_run_layers(const char* pattern, int N, const void* const* 
                     k_scale ? k_scale[l] : nullptr, w[l], L, H, D, topk, dt, tcache, nullptr, nullptr,
                     workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
       st = launch_prefill(a);
+      if (st != DSA_OK) {
+        std::string m = g_err;
+        return fail(st, "layer %d: %s", l, m.c_str());
+      }
+    }
+    if (hook) hook(l, src[l], tcache, stream, user);
+  }
+  if (src_layer_out) memcpy(src_layer_out, src.data(), sizeof(int32_t) * (size_t)N);
+  return ok();
+}
+
+dsa_status indexcache_run_decode_layers(const char* pattern, int N, const uint16_t* const* q,
+                                        const uint16_t* const* w, const uint8_t* const* k_cache,
+                                        const float* const* k_scale, const int32_t* seq_lens, int B, int Lmax,
+                                        int H, int D, int topk, int32_t* tcache, int32_t* src_layer_out,
+                                        indexcache_layer_fn hook, void* user, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  std::vector<int32_t> src((size_t)(N > 0 ? N : 1));
+  dsa_status st = indexcache_resolve(pattern, N, src.data());
+  if (st != DSA_OK) return st;
+  if (!q || !w || !k_cache || !k_scale)
+    return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache and k_scale pointer arrays must not be NULL");
+  if (!tcache) return fail(DSA_ERR_INVALID_ARG, "tcache must not be NULL");
+  auto args = [&](int l) {
+    return DecodeArgs{q[l], w[l], k_cache[l], k_scale[l], seq_lens, B, Lmax, H, D, topk, tcache, nullptr,
+                      workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  };
+  // validate every F layer before enqueueing anything
+  for (int l = 0; l < N; ++l) {
+    if (pattern[l] != 'F') continue;
+    st = validate_decode(args(l));
+    if (st != DSA_OK) {
+      std::string m = g_err;
+      return fail(st, "layer %d: %s", l, m.c_str());
+    }
+  }
+  for (int l = 0; l < N; ++l) {
+    if (pattern[l] == 'F') {
+      st = launch_decode(args(l));
       if (st != DSA_OK) {
         std::string m = g_err;
         return fail(st, "layer %d: %s", l, m.c_str());

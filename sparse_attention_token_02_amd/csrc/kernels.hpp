@@ -56,6 +56,9 @@ struct DecodeWsSizes {
   size_t hist_words, bitmap_words, cand_cnt;
 };
 
+// Largest key index the overlap kernel counts; larger entries are ignored.
+constexpr int OVERLAP_MAX_KEY = (1 << 30) - 1;
+
 struct OverlapParams {
   const int32_t* idx[OVERLAP_MAX_N];   // N device pointers, each [L, topk]
   int N;

@@ -8,8 +8,10 @@
 // Integer counts summed with atomic adds: the result does not depend on the
 // order in which rows are processed.
 //
-// A workgroup handles a strided subset of the rows.  The key range [0, t] of
-// a row is cut into windows of 8192 keys; for each window every layer's keys
+// A workgroup handles a strided subset of the rows.  The key range of a row,
+// [0, largest index any layer holds in it] (at most [0, t] for a causal
+// prefill row, [0, len_b) for a decode row), is cut into windows of 8192
+// keys; for each window every layer's keys
 // are set in an LDS bitmap (the range of each sorted list that falls in the
 // window is found by binary search), then every thread ANDs and popcounts the
 // bitmaps of its layer pairs and keeps the running counts in registers until
@@ -38,7 +40,7 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
 
 __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
   extern __shared__ uint32_t bms[];          // [N][OV_WWORDS]
-  __shared__ int rng_lo[OVERLAP_MAX_N], rng_hi[OVERLAP_MAX_N], valid_n[OVERLAP_MAX_N];
+  __shared__ int rng_lo[OVERLAP_MAX_N], rng_hi[OVERLAP_MAX_N], valid_n[OVERLAP_MAX_N], last_key[OVERLAP_MAX_N];
   const int tid = threadIdx.x;
   const int N = p.N;
   const int P = N * (N + 1) / 2;
@@ -76,9 +78,14 @@ __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
         else hi = mid;
       }
       valid_n[tid] = lo;
+      last_key[tid] = lo > 0 ? row[lo - 1] : -1;   // rows are ascending
     }
     __syncthreads();
-    const int nwin = (t + 1 + OV_WBITS - 1) / OV_WBITS;
+    int kmax = -1;
+    for (int i = 0; i < N; ++i) kmax = max(kmax, last_key[i]);
+    kmax = min(kmax, OVERLAP_MAX_KEY);
+    __syncthreads();   // every thread has read last_key before the next row rewrites it
+    const int nwin = (kmax + OV_WBITS) / OV_WBITS;   // windows covering [0, kmax]
     for (int win = 0; win < nwin; ++win) {
       const int v0 = win * OV_WBITS;
       for (int i = tid; i < N * OV_WWORDS; i += OV_NT) bms[i] = 0u;
@@ -97,7 +104,7 @@ __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
         }
       }
       __syncthreads();
-      const int nwords = min(OV_WWORDS, (t + 1 - v0 + 31) >> 5);
+      const int nwords = min(OV_WWORDS, (kmax + 1 - v0 + 31) >> 5);
 #pragma unroll
       for (int u = 0; u < OV_PPT; ++u) {
         if (pi[u] >= 0) {

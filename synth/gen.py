@@ -34,7 +34,7 @@ import numpy as np
 __all__ = [
     "GAMMA", "mix64_int", "stream_base", "hash_u64", "NORMAL_TABLE", "normal_f32",
     "uniform_int", "bf16_bits", "e4m3_bits", "quant_rows_e4m3", "heavy_positions",
-    "STREAM", "CONFIGS", "prefill_inputs", "decode_inputs", "fs_layer_inputs",
+    "STREAM", "CONFIGS", "prefill_inputs", "decode_inputs", "fs_layer_inputs", "fs_decode_layer_inputs",
     "fs_noise_rows", "decode_lens", "FS_PATTERNS", "ragged_decode_config",
 ]
 
@@ -166,6 +166,9 @@ CONFIGS = {
     # 47-layer reuse schedule at L=65536, correlated layers
     "fs_47": dict(kind="fs", N=47, L=65536, H=64, D=128, topk=2048, dtype="fp8", seed=0,
                   rho=0.9, sigma=0.44, w_div=8.0),
+    # one decode step through 47 correlated layers, 32 sequences x 131072 cached tokens
+    "fs_decode_47": dict(kind="fs_decode", N=47, B=32, Lmax=131072, H=64, D=128, topk=2048, seed=0,
+                         ragged=False, rho=0.9, sigma=0.44, w_div=8.0),
     # L=196608 fp8 prefill, 1% heavy keys at 3x
     "prefill_196k": dict(kind="prefill", L=196608, H=64, D=128, topk=2048, dtype="fp8", seed=0,
                          heavy_count=round(0.01 * 196608), heavy_factor=3.0, w_div=8.0),
@@ -288,6 +291,25 @@ def fs_layer_inputs(cfg: dict, layer: int, rows=None, with_keys: bool = True) ->
     W = fs_noise_rows(cfg, "w", layer, rows, H) / _F32(cfg["w_div"])
     out["w"] = bf16_bits(W.astype(np.float32))
     return out
+
+
+def fs_decode_layer_inputs(cfg: dict, layer: int, seqs=None) -> dict:
+    """Host-side inputs of one layer of the decode layer-reuse workload, for
+    sequences ``seqs`` (all by default): the decode tensors of
+    ``decode_inputs`` (e4m3 cache with per-token scales, bf16 q and w), where
+    the cache rows (sequence b, token s: row b*Lmax + s), q and w all follow
+    the layer recurrence of ``fs_noise_rows``.  ``lens`` is shared by all layers."""
+    B, Lmax, H, D = cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"]
+    seqs = np.arange(B, dtype=np.int64) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    S = len(seqs)
+    cache = np.empty((S, Lmax, D), dtype=np.uint8)
+    kscale = np.empty((S, Lmax), dtype=np.float32)
+    for i, b in enumerate(seqs):
+        K = fs_noise_rows(cfg, "k", layer, int(b) * Lmax + np.arange(Lmax, dtype=np.int64), D)
+        cache[i], kscale[i] = quant_rows_e4m3(K)
+    q = bf16_bits(fs_noise_rows(cfg, "q", layer, seqs, H * D)).reshape(S, H, D)
+    w = bf16_bits((fs_noise_rows(cfg, "w", layer, seqs, H) / _F32(cfg["w_div"])).astype(np.float32))
+    return {"cache": cache, "k_scale": kscale, "q": q, "w": w, "lens": decode_lens(cfg)[seqs], "seqs": seqs}
 
 
 def fs_keys_by_layer(cfg: dict, last_layer: int):

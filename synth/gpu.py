@@ -181,3 +181,20 @@ class DeviceGen:
             del Q
         W = self.rows_f32(seed, "w", L, H, div=cfg["w_div"], **rs)
         return {"q": q, "q_scale": qs, "k": k, "k_scale": k_scale, "w": self.bf16(W)}
+
+    def fs_decode_layer_inputs(self, cfg: dict, layer: int) -> dict:
+        torch = self.torch
+        B, Lmax, H, D, seed = cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"], cfg["seed"]
+        rs = dict(layers=layer, rho=cfg["rho"], sigma=cfg["sigma"])
+        cache = torch.empty((B, Lmax, D), dtype=torch.uint8, device=self.device)
+        ks = torch.empty((B, Lmax), dtype=torch.float32, device=self.device)
+        for b in range(B):
+            K = self.rows_f32(seed, "k", Lmax, D, row0=b * Lmax, **rs)
+            c, s = self.quant_e4m3(K)
+            cache[b] = c
+            ks[b] = s
+            del K
+        q = self.bf16(self.rows_f32(seed, "q", B, H * D, **rs)).view(B, H, D)
+        w = self.bf16(self.rows_f32(seed, "w", B, H, div=cfg["w_div"], **rs))
+        lens = torch.from_numpy(gen.decode_lens(cfg)).to(self.device)
+        return {"cache": cache, "k_scale": ks, "q": q, "w": w, "lens": lens}

@@ -168,6 +168,29 @@ def test_run_layers_rejects_before_any_device_call():
     assert call(qq=q_s_null, wsb=16) == dsa.DSA_ERR_WORKSPACE
 
 
+def test_run_decode_layers_rejects_before_any_device_call():
+    lib = dsa.lib()
+    P = ctypes.c_void_p * 3
+    arr = lambda *v: P(*v)
+    full = arr(FAKE, FAKE, FAKE)
+    hook = dsa.HOOK_T()
+
+    def call(pattern=b"FSF", N=3, tc=FAKE, wsb=1 << 30, qq=full, H=64, cache=full):
+        return lib.indexcache_run_decode_layers(pattern, N, qq, full, cache, full, FAKE, 2, 1024, H, 128, 16, tc,
+                                                None, hook, None, FAKE, wsb, None)
+    assert call(pattern=b"SFF") == dsa.DSA_ERR_INVALID_ARG
+    assert call(pattern=b"FXF") == dsa.DSA_ERR_INVALID_ARG
+    assert call(N=2) == dsa.DSA_ERR_INVALID_ARG
+    assert call(tc=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
+    assert "layer 0" in dsa.dsa_last_error()
+    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(qq=arr(FAKE, FAKE, None)) == dsa.DSA_ERR_INVALID_ARG     # layer 2 is F and has no q
+    assert "layer 2" in dsa.dsa_last_error()
+    assert call(cache=arr(FAKE, FAKE, FAKE + 8)) == dsa.DSA_ERR_INVALID_ARG   # misaligned cache of layer 2
+    assert call(qq=arr(FAKE, None, FAKE), cache=arr(FAKE, None, FAKE), wsb=16) == dsa.DSA_ERR_WORKSPACE
+
+
 def test_one_hip_runtime_in_process():
     """The library binds to the HIP runtime torch loaded (never a second copy)."""
     import torch  # noqa: F401

@@ -49,6 +49,30 @@ def test_overlap_matches_oracle_exactly(dsa, N, L, k, rows):
         assert ratio[1, 2] == ratio[1, 1]
 
 
+def test_overlap_of_decode_rows_matches_oracle(dsa):
+    """Decode-shaped rows: one row per sequence, keys far beyond the row
+    number (up to 131071), short rows padded with -1, one empty row."""
+    import torch
+    rng = np.random.default_rng(5)
+    N, R, k = 7, 40, 512
+    sets = np.full((N, R, k), -1, dtype=np.int32)
+    for b in range(R - 1):
+        n = int(rng.integers(k // 2, 131072))
+        base = np.sort(rng.choice(n, size=min(k, n), replace=False))
+        for i in range(N):
+            keep = base.copy()
+            swap = rng.random(len(keep)) < 0.3 * i / N       # layers drift apart
+            keep[swap] = rng.choice(n, size=int(swap.sum()), replace=True)
+            keep = np.unique(keep)[:k]
+            sets[i, b, :len(keep)] = keep
+    note("overlap decode rows N=7 R=40 k=512")
+    counts, ratio = dsa.topk_overlap_matrix([dev(sets[i]) for i in range(N)], k, row_begin=0, row_end=R)
+    torch.cuda.synchronize()
+    want = oracle.overlap_counts([sets[i] for i in range(N)], range(R))
+    assert np.array_equal(counts.cpu().numpy().astype(np.uint64), want)
+    assert 0.5 < ratio[0, 1] < 1.0 and ratio[0, N - 1] < ratio[0, 1]
+
+
 def test_overlap_closed_form(dsa):
     import torch
     L, k = 5000, 128
@@ -106,3 +130,51 @@ def test_fs_driver_reuses_cache_in_place(dsa):
         got = host(seen[l][3])
         for r, t in enumerate(rows):
             assert parity.check_row(got[t], res["o"][r], res["A"][r], cfg["topk"]) is None, (l, t)
+
+
+def test_fs_decode_driver_matches_oracle(dsa):
+    """One decode step through the F/S schedule: every F layer's selection
+    equals the oracle's for every sequence, S layers hand on their source's
+    buffer unchanged, and an F layer equals a standalone decode call."""
+    import torch
+    cfg = dict(gen.CONFIGS["fs_decode_47"], B=3, Lmax=3000, topk=256, ragged=True)
+    pattern = "FSSFSF"
+    N, B, topk = len(pattern), cfg["B"], cfg["topk"]
+    note("fs decode driver 6 layers B=3 Lmax=3000 k=256")
+    hl = [gen.fs_decode_layer_inputs(cfg, l) if pattern[l] == "F" else None for l in range(N)]
+    dl = [{key: dev(v) for key, v in h.items() if key != "seqs"} if h else None for h in hl]
+    pick = lambda key: [dl[l][key] if dl[l] else None for l in range(N)]
+    lens = dl[0]["lens"]
+    seen = []
+
+    def hook(layer, src, tcache):
+        seen.append((layer, src, tcache.data_ptr(), tcache.clone()))
+
+    tcache, src = dsa.indexcache_run_decode_layers(pattern, pick("q"), pick("w"), pick("cache"), pick("k_scale"),
+                                                   lens, topk, hook=hook)
+    torch.cuda.synchronize()
+    assert src == oracle.fs_resolve(pattern)
+    assert [s[0] for s in seen] == list(range(N)) and [s[1] for s in seen] == src
+    assert len(set(s[2] for s in seen)) == 1 and seen[0][2] == tcache.data_ptr()
+    want, osrc, calls = oracle.fs_run(pattern, lambda l: oracle.decode(
+        hl[l]["q"], hl[l]["w"], hl[l]["cache"], hl[l]["k_scale"], hl[l]["lens"], topk, return_scores=True))
+    assert osrc == src and calls == pattern.count("F")
+    for l in range(N):
+        got = host(seen[l][3])
+        for b in range(B):
+            assert parity.check_row(got[b], want[l]["o"][b], want[l]["A"][b], topk) is None, (l, b)
+        if pattern[l] == "S":
+            assert torch.equal(seen[l][3], seen[src[l]][3]), l
+        else:
+            alone, _ = dsa.dsa_indexer_topk_decode(dl[l]["q"], dl[l]["w"], dl[l]["cache"], dl[l]["k_scale"], lens,
+                                                   topk)
+            torch.cuda.synchronize()
+            assert torch.equal(alone, seen[l][3]), l
+    # the layers differ, so the S layers really did reuse rather than recompute
+    assert not torch.equal(seen[0][3], seen[3][3])
+    # overlap of the per-layer decode selections (rows are sequences)
+    counts, _ = dsa.topk_overlap_matrix([s[3] for s in seen], topk, row_begin=0, row_end=B, ratio=False)
+    torch.cuda.synchronize()
+    want_c = oracle.overlap_counts([want[l]["idx"] for l in range(N)], range(B))
+    assert np.array_equal(counts.cpu().numpy().astype(np.uint64), want_c)
+    assert want_c[0, 3] > 0

@@ -54,3 +54,13 @@ def test_decode_small_identical(g):
     h = gen.decode_inputs(cfg)
     for key in ("cache", "k_scale", "q", "w", "lens"):
         assert np.array_equal(host(d[key]), h[key]), key
+
+
+def test_fs_decode_layer_recurrence_identical(g):
+    cfg = dict(gen.CONFIGS["fs_decode_47"], B=3, Lmax=1500, ragged=True)
+    note("synth fs decode layers 0, 3")
+    for layer in (0, 3):
+        d = g.fs_decode_layer_inputs(cfg, layer)
+        h = gen.fs_decode_layer_inputs(cfg, layer)
+        for key in ("cache", "k_scale", "q", "w", "lens"):
+            assert np.array_equal(host(d[key]), h[key]), (layer, key)

@@ -127,3 +127,17 @@ def test_fs_recurrence_rows_consistent():
     x3 = gen.fs_noise_rows(cfg, "k", 3, np.arange(2000), 64).ravel()
     c = np.corrcoef(x2, x3)[0, 1]
     assert abs(c - 0.9 / np.sqrt(0.81 + 0.44**2)) < 0.01
+
+
+def test_fs_decode_layer_zero_is_the_decode_recipe():
+    """Layer 0 of the decode layer-reuse workload draws the same streams and
+    rows as the single-layer decode recipe, so the two agree bit for bit."""
+    cfg = dict(gen.CONFIGS["fs_decode_47"], B=3, Lmax=700, ragged=True)
+    a = gen.fs_decode_layer_inputs(cfg, 0)
+    b = gen.decode_inputs(cfg)
+    for key in ("cache", "k_scale", "q", "w", "lens"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    c = gen.fs_decode_layer_inputs(cfg, 2, seqs=[1])
+    d = gen.fs_decode_layer_inputs(cfg, 2)
+    for key in ("cache", "k_scale", "q", "w", "lens"):
+        np.testing.assert_array_equal(c[key][0], d[key][1], err_msg=key)
