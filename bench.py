@@ -11,7 +11,7 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|fs_47|fs_decode_47``) print their own line.
+(``--workload tiny|prefill_196k|fs_47|fs_decode_47|mli_decode_47``) print their own line.
 """
 from __future__ import annotations
 
@@ -251,6 +251,8 @@ def run_workload(args):
         return run_fs(args, g, dsa, gen, stream)
     if name == "fs_decode_47":
         return run_fs_decode(args, g, dsa, gen, stream)
+    if name == "mli_decode_47":
+        return run_mli_decode(args, g, dsa, gen, stream)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -349,6 +351,78 @@ def run_fs_decode(args, g, dsa, gen, stream):
         if s_layers:
             res.setdefault("s_layer_mean_overlap_with_source", {})[pname] = round(
                 float(sum(ratio[l, src[l]] for l in s_layers) / len(s_layers)), 4)
+    return res
+
+
+def run_mli_decode(args, g, dsa, gen, stream):
+    """One decode step (32 sequences x 131072 cached tokens, 47 layers) with a
+    stand-in sparse attention per layer (one head over the k selected rows of
+    a 576-value bf16 latent cache; four latent caches, 19.3 GB, cycled over
+    the layers): per pattern, the indexers alone, IndexCache with each
+    layer's attention after its indexer on one stream, and the lagged
+    (multi-layer indexer) schedule with the indexers on a second stream."""
+    import math
+    import torch
+    cfg = gen.CONFIGS["fs_decode_47"]
+    N, B, Lmax, H, D, topk, seed = cfg["N"], cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"], cfg["topk"], cfg["seed"]
+    dev = g.device
+    log("generating 47 decode layers, 4 latent caches")
+    layers = [g.fs_decode_layer_inputs(cfg, l) for l in range(N)]
+    lens = layers[0]["lens"]
+    NLAT = 4
+    lat = [g.standin_latent(seed, i, B, Lmax) for i in range(NLAT)]
+    qa = [g.standin_query(seed, l, B) for l in range(N)]
+    scale = 1.0 / math.sqrt(576.0)
+    ws = torch.empty(dsa.dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dtype=torch.uint8, device=dev)
+    aws = torch.empty(dsa.standin_sparse_attention_workspace(B, topk), dtype=torch.uint8, device=dev)
+    aout = torch.empty((B, 512), dtype=torch.float32, device=dev)
+    tcache = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    sel_buf = torch.empty((N, B, topk), dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    pick = lambda key: [layers[l][key] for l in range(N)]
+
+    def attention(layer, sel):
+        dsa.standin_sparse_attention(qa[layer], lat[layer % NLAT], sel, scale, out=aout, workspace=aws, stream=stream)
+
+    def indexers(pat):
+        dsa.indexcache_run_decode_layers(pat, pick("q"), pick("w"), pick("cache"), pick("k_scale"), lens, topk,
+                                         tcache=tcache, workspace=ws, stream=stream)
+
+    def serial(pat):
+        dsa.indexcache_run_decode_layers(pat, pick("q"), pick("w"), pick("cache"), pick("k_scale"), lens, topk,
+                                         tcache=tcache, hook=lambda l, s, tc: attention(l, tc), workspace=ws,
+                                         stream=stream)
+
+    def lagged(pat):
+        dsa.indexcache_run_decode_layers_mli(pat, pick("q"), pick("w"), pick("cache"), pick("k_scale"), lens, topk,
+                                             sel_buf=sel_buf, attn=lambda l, s, sel: attention(l, sel),
+                                             workspace=ws, stream=stream, side_stream=side)
+
+    def attention_only():
+        for l in range(N):
+            attention(l, tcache)
+
+    steps, warm = max(1, args.steps), max(0, args.warmup)
+    avg = lambda ms: sum(ms) / len(ms) * 1e3
+    indexers(gen.FS_PATTERNS["all_F"])           # a real selection in tcache for attention_only
+    att_us = avg(time_calls(attention_only, steps, warm, stream))
+    res = {"metric": METRIC, "workload": "mli_decode_47",
+           "config": {"workload": "mli_decode_47", "N": N, "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
+                      "attention": "stand-in, 1 head, 576-value bf16 latent rows"},
+           "attention_us_per_layer": round(att_us / N, 2), "step_us": {}, "lagged_speedup": {}}
+    for pname, pat in gen.FS_PATTERNS.items():
+        t_idx = avg(time_calls(lambda: indexers(pat), steps, warm, stream))
+        t_ser = avg(time_calls(lambda: serial(pat), steps, warm, stream))
+        t_mli = avg(time_calls(lambda: lagged(pat), steps, warm, stream))
+        res["step_us"][pname] = {"indexers_only": round(t_idx, 1), "indexcache_serial": round(t_ser, 1),
+                                 "lagged_two_streams": round(t_mli, 1)}
+        res["lagged_speedup"][pname] = round(t_ser / t_mli, 4)
+    per_layer = decode_bytes(gen.decode_lens(cfg), H, D, topk, B)
+    t_all = res["step_us"]["all_F"]["lagged_two_streams"] * 1e-6
+    gbps = N * per_layer / t_all / 1e9
+    res.update({"value": round(gbps, 1), "unit": "GB/s",
+                "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None}})
     return res
 
 

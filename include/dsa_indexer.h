@@ -194,6 +194,71 @@ dsa_status indexcache_run_decode_layers(const char* pattern, int N,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-layer Indexer (lagged) decode schedule.  [ML] abstract: adjacent
+ * layers select nearly the same tokens, so a layer attends the selection of
+ * the previous indexer layer instead of its own; its own indexer then runs
+ * concurrently with its attention.  Composed with F/S: S layers have no
+ * indexer and attend the nearest earlier F layer's selection, as before.
+ * ------------------------------------------------------------------------ */
+
+/* Host only, no device work.  attn_src (host [N], may be NULL) receives the
+ * layer whose selection layer l attends: the last F layer strictly before l,
+ * or l itself when there is none (the first layer).  The pattern rules are
+ * those of indexcache_resolve. */
+dsa_status mli_resolve(const char* pattern, int N, int32_t* attn_src);
+
+/*
+ * One decode step through the lagged schedule, on two streams.  F layers run
+ * dsa_indexer_topk_decode (inputs as in indexcache_run_decode_layers) on
+ * `side_stream`, the i-th F layer into slot i of sel_buf; for every layer l,
+ * in order, `attn(l, attn_src[l], selection, stream, user)` is called on the
+ * host and enqueues that layer's attention on `stream` (the main one).
+ * Ordering, by events (device scope, no system fence):
+ *  - the side stream starts after the work already queued on `stream`;
+ *  - layer l's attention waits for the indexer that wrote its selection;
+ *  - on return, `stream` waits for the side stream's last work.
+ * Every F layer has a slot of its own, so the indexers never wait for the
+ * attention: each one overlaps the attention of the layers before it (and
+ * whatever the caller enqueues on `stream` in between), and the whole step
+ * is ordered on `stream`.
+ * sel_buf        [F, B, topk] int32, caller-owned, F = number of F layers in
+ *                the pattern; after the step slot i holds the i-th F layer's
+ *                selection.  The `selection` pointer handed to attn is one
+ *                slot.
+ * attn_src_out   host [N] or NULL; attn may be NULL.
+ * side_stream    another hipStream_t of the same device (the same stream as
+ *                `stream`, or both NULL, gives a correct but serial schedule).
+ * Every F layer is validated before anything is enqueued.  Four events are
+ * created per call and released on return.
+ */
+dsa_status indexcache_run_decode_layers_mli(const char* pattern, int N,
+                                            const uint16_t* const* q, const uint16_t* const* w,
+                                            const uint8_t* const* k_cache, const float* const* k_scale,
+                                            const int32_t* seq_lens, int B, int Lmax, int H, int D, int topk,
+                                            int32_t* sel_buf, int32_t* attn_src_out,
+                                            indexcache_layer_fn attn, void* user,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream, void* side_stream);
+
+/*
+ * Stand-in consumer of a decode selection for the schedules above: one head
+ * of sparse softmax attention per sequence over the selected rows of a bf16
+ * latent cache (576 values per row, the first 512 of which are the value),
+ * with the memory traffic of sparse MLA decode ([ML] abstract: each layer
+ * attends only the k selected tokens).  It is not a model's attention layer.
+ *   s_j = scale * q[b] . latent[b, T_j, 0:576]
+ *   out[b] = sum_j softmax(s)_j latent[b, T_j, 0:512]
+ * over the entries 0 <= T_j < Lmax of sel[b] (others, such as -1 padding,
+ * are skipped; a row with none gives zeros).
+ * q [B, 576] bf16, latent [B, Lmax, 576] bf16, sel [B, topk] int32,
+ * out [B, 512] fp32, all device, q/latent/out 16-byte aligned.
+ */
+dsa_status standin_sparse_attention_workspace(int B, int topk, size_t* bytes);
+dsa_status standin_sparse_attention(const uint16_t* q, const uint16_t* latent, const int32_t* sel,
+                                    int B, int Lmax, int topk, float scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Cross-layer overlap.  [IC] 1.2.
  * ------------------------------------------------------------------------ */
 

@@ -17,7 +17,12 @@ Sources (the pages are cited by title and section):
   nearest earlier F layer, f(l) = max{j < l : c_j = F}; the first layer is
   always F.
 * Multi-layer Indexer abstract (equalang.com): at decode the indexer scores
-  the whole cache of the sequence and keeps the k = 2048 highest.
+  the whole cache of the sequence and keeps the k = 2048 highest.  Adjacent
+  layers select nearly the same tokens, so in the lagged schedule a layer
+  attends the selection of the previous indexer layer instead of its own,
+  which lets its own indexer run beside its attention; with IndexCache, S
+  layers keep attending the nearest earlier F layer's selection.  Each layer
+  attends only its k selected tokens.
 
 Readings where the pages are silent: the diagonal s = t is part of the
 prefix; ties are broken towards the lower key index (a total order: score
@@ -25,7 +30,8 @@ descending, then index ascending); selected
 indices are returned in ascending order and padded with -1 when fewer than k
 keys exist; FP8 is OCP e4m3fn with one fp32 scale per token, applied by
 dequantising before scoring; the decode query sits at position len-1 and its
-own key is already in the cache.
+own key is already in the cache; in the lagged schedule the first layer,
+having no earlier indexer layer, attends its own selection.
 
 Parity status: every function here is pinned by tests in ``tests/`` that do
 not reuse its code (closed forms, invariants, brute force, a hand-worked
@@ -37,7 +43,8 @@ import numpy as np
 
 __all__ = [
     "dec_e4m3", "dec_bf16", "dequant", "indexer_scores", "select_topk",
-    "prefill", "decode", "fs_resolve", "fs_run", "overlap_counts", "overlap_ratio",
+    "prefill", "decode", "fs_resolve", "fs_run", "mli_resolve", "mli_run", "standin_attention",
+    "overlap_counts", "overlap_ratio",
 ]
 
 
@@ -216,6 +223,57 @@ def fs_run(pattern: str, layer_topk):
             calls += 1
         outs.append(cache)
     return outs, src, calls
+
+
+def mli_resolve(pattern: str) -> list[int]:
+    """Lagged (multi-layer indexer) schedule: the layer whose selection layer l
+    attends -- the last F layer strictly before l, or l itself when no F layer
+    precedes it (the first layer).  Pattern rules as in ``fs_resolve``."""
+    fs_resolve(pattern)   # validates
+    src = []
+    prev_f = None
+    for l, c in enumerate(pattern):
+        src.append(l if prev_f is None else prev_f)
+        if c == "F":
+            prev_f = l
+    return src
+
+
+def mli_run(pattern: str, layer_topk):
+    """Run the lagged schedule: ``layer_topk(l)`` gives layer l's own indices
+    (F layers only).  Returns (the selection each layer attends, attn_src,
+    number of indexer calls)."""
+    asrc = mli_resolve(pattern)
+    own = {}
+    for l, c in enumerate(pattern):
+        if c == "F":
+            own[l] = layer_topk(l)
+    return [own[asrc[l]] for l in range(len(pattern))], asrc, len(own)
+
+
+# ----------------------------------------------------------------------------
+# Stand-in consumer: one head of sparse softmax attention
+# ----------------------------------------------------------------------------
+
+def standin_attention(q, latent, sel, scale: float) -> np.ndarray:
+    """Per sequence b: softmax over the selected rows j (entries 0 <= T_j <
+    Lmax of sel[b]) of scale * q[b] . latent[b, T_j, :576], applied to the
+    value part latent[b, T_j, :512].  q [B,576] and latent [B,Lmax,576] are
+    bf16 bits; returns float64 [B,512] (zeros for a row with no entry)."""
+    q = np.asarray(q)
+    latent = np.asarray(latent)
+    sel = np.asarray(sel)
+    B, Lmax = latent.shape[0], latent.shape[1]
+    out = np.zeros((B, 512), dtype=np.float64)
+    for b in range(B):
+        rows = sel[b][(sel[b] >= 0) & (sel[b] < Lmax)]
+        if len(rows) == 0:
+            continue
+        X = dec_bf16(latent[b, rows])                 # [n, 576]
+        s = float(scale) * (X @ dec_bf16(q[b]))       # [n]
+        p = np.exp(s - s.max())
+        out[b] = (p / p.sum()) @ X[:, :512]
+    return out
 
 
 # ----------------------------------------------------------------------------

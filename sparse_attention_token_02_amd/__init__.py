@@ -29,7 +29,9 @@ EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
     "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill",
     "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode",
-    "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers", "topk_overlap_matrix",
+    "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers", "mli_resolve",
+    "indexcache_run_decode_layers_mli", "standin_sparse_attention_workspace", "standin_sparse_attention",
+    "topk_overlap_matrix",
 )
 
 if not os.path.exists(LIB_PATH):
@@ -66,6 +68,17 @@ _lib.indexcache_run_decode_layers.argtypes = [ctypes.c_char_p, _i32, ctypes.POIN
                                               ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _i32, _i32, _i32,
                                               _i32, _i32, _vp, ctypes.POINTER(ctypes.c_int32), HOOK_T, _vp, _vp,
                                               _sz, _vp]
+_lib.mli_resolve.restype = _i32
+_lib.mli_resolve.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(ctypes.c_int32)]
+_lib.indexcache_run_decode_layers_mli.restype = _i32
+_lib.indexcache_run_decode_layers_mli.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                  ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _i32, _i32, _i32,
+                                                  _i32, _i32, _vp, ctypes.POINTER(ctypes.c_int32), HOOK_T, _vp,
+                                                  _vp, _sz, _vp, _vp]
+_lib.standin_sparse_attention_workspace.restype = _i32
+_lib.standin_sparse_attention_workspace.argtypes = [_i32, _i32, ctypes.POINTER(_sz)]
+_lib.standin_sparse_attention.restype = _i32
+_lib.standin_sparse_attention.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
 _lib.topk_overlap_matrix.restype = _i32
 _lib.topk_overlap_matrix.argtypes = [ctypes.POINTER(_vp), _i32, _i32, _i32, _i64, _i64, _i64, _vp,
                                      ctypes.POINTER(ctypes.c_double), _vp]
@@ -261,6 +274,78 @@ def indexcache_run_decode_layers(pattern: str, q, w, k_cache, k_scale, seq_lens,
     if errors:
         raise errors[0]
     return tcache, list(src[:N])
+
+
+def mli_resolve(pattern: str) -> list[int]:
+    N = len(pattern)
+    src = (ctypes.c_int32 * max(N, 1))()
+    _check(_lib.mli_resolve(pattern.encode(), N, src))
+    return list(src[:N])
+
+
+def indexcache_run_decode_layers_mli(pattern: str, q, w, k_cache, k_scale, seq_lens, topk: int, *, sel_buf=None,
+                                     attn=None, workspace=None, stream=None, side_stream=None):
+    """One decode step through the lagged (multi-layer indexer) schedule.
+    Per-layer lists as in ``indexcache_run_decode_layers``.  ``attn(layer,
+    src_layer, selection)`` runs on the host for every layer, in order, with
+    ``selection`` the [B, topk] slot of ``sel_buf`` that layer attends; work it
+    enqueues on ``stream`` (the current stream by default) is ordered after
+    that selection is written.  ``side_stream`` (a torch stream) runs the
+    indexers.  Returns (sel_buf [F, B, topk], slot i = the i-th F layer's
+    selection, attn_src list)."""
+    import torch
+    N = len(pattern)
+    f0 = next(i for i, c in enumerate(pattern) if c == "F") if "F" in pattern else 0
+    B, H, D = q[f0].shape
+    Lmax = k_cache[f0].shape[1]
+    dev = q[f0].device
+    nf = pattern.count("F")
+    if sel_buf is None:
+        sel_buf = torch.empty((max(nf, 1), B, topk), dtype=torch.int32, device=dev)
+    if sel_buf.shape[0] < nf or tuple(sel_buf.shape[1:]) != (B, topk) or not sel_buf.is_contiguous():
+        raise ValueError(f"sel_buf must be a contiguous [{nf}+, {B}, {topk}] int32 tensor")
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace)
+    if side_stream is None:
+        side_stream = torch.cuda.Stream(device=dev)
+    src = (ctypes.c_int32 * max(N, 1))()
+    slots = {sel_buf[i].data_ptr(): sel_buf[i] for i in range(sel_buf.shape[0])}
+    errors = []
+
+    def _hook(layer, src_layer, idx_ptr, stream_ptr, user):
+        try:
+            attn(layer, src_layer, slots[idx_ptr])
+        except Exception as e:  # surfaced after the call returns
+            errors.append(e)
+
+    cb = HOOK_T(_hook) if attn is not None else HOOK_T()
+    _check(_lib.indexcache_run_decode_layers_mli(
+        pattern.encode(), N, _ptr_array(q), _ptr_array(w), _ptr_array(k_cache), _ptr_array(k_scale),
+        _ptr(seq_lens), B, Lmax, H, D, topk, _ptr(sel_buf), src, cb, None, _ptr(ws), ws.numel(),
+        _stream(stream), _stream(side_stream)))
+    if errors:
+        raise errors[0]
+    return sel_buf, list(src[:N])
+
+
+def standin_sparse_attention_workspace(B: int, topk: int) -> int:
+    n = _sz(0)
+    _check(_lib.standin_sparse_attention_workspace(B, topk, ctypes.byref(n)))
+    return n.value
+
+
+def standin_sparse_attention(q, latent, sel, scale: float, *, out=None, workspace=None, stream=None):
+    """q [B,576] bf16, latent [B,Lmax,576] bf16, sel [B,topk] int32 (device).
+    Returns out [B,512] fp32."""
+    import torch
+    B = q.shape[0]
+    Lmax = latent.shape[1]
+    topk = sel.shape[1]
+    if out is None:
+        out = torch.empty((B, 512), dtype=torch.float32, device=q.device)
+    ws = _workspace(standin_sparse_attention_workspace(B, topk), q.device, workspace)
+    _check(_lib.standin_sparse_attention(_ptr(q), _ptr(latent), _ptr(sel), B, Lmax, topk, float(scale), _ptr(out),
+                                         _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def topk_overlap_matrix(idx, topk: int, *, row_begin=None, row_end=None, row_stride: int = 1,

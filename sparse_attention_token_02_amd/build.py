@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdsa_indexer.so")
-SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "overlap.hip"]
+SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "overlap.hip", "attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

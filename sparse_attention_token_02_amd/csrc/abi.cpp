@@ -234,6 +234,23 @@ dsa_status launch_decode(const DecodeArgs& a) {
   return DSA_OK;
 }
 
+// Events of one call; destroyed on return (a pending event is released by
+// the runtime once it completes).
+struct EventSet {
+  hipEvent_t ev[4] = {};
+  int n = 0;
+  ~EventSet() {
+    for (int i = 0; i < n; ++i) hipEventDestroy(ev[i]);
+  }
+  hipError_t create(int count, unsigned flags) {
+    for (; n < count; ++n) {
+      hipError_t e = hipEventCreateWithFlags(&ev[n], flags);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -384,6 +401,112 @@ dsa_status indexcache_run_decode_layers(const char* pattern, int N, const uint16
     if (hook) hook(l, src[l], tcache, stream, user);
   }
   if (src_layer_out) memcpy(src_layer_out, src.data(), sizeof(int32_t) * (size_t)N);
+  return ok();
+}
+
+dsa_status mli_resolve(const char* pattern, int N, int32_t* attn_src) {
+  std::vector<int32_t> src((size_t)(N > 0 ? N : 1));
+  dsa_status st = indexcache_resolve(pattern, N, src.data());
+  if (st != DSA_OK) return st;
+  int prev_f = -1;   // last F layer strictly before l
+  for (int l = 0; l < N; ++l) {
+    if (attn_src) attn_src[l] = prev_f >= 0 ? prev_f : l;
+    if (pattern[l] == 'F') prev_f = l;
+  }
+  return ok();
+}
+
+dsa_status indexcache_run_decode_layers_mli(const char* pattern, int N, const uint16_t* const* q,
+                                            const uint16_t* const* w, const uint8_t* const* k_cache,
+                                            const float* const* k_scale, const int32_t* seq_lens, int B,
+                                            int Lmax, int H, int D, int topk, int32_t* sel_buf,
+                                            int32_t* attn_src_out, indexcache_layer_fn attn, void* user,
+                                            void* workspace, size_t workspace_bytes, void* stream,
+                                            void* side_stream) {
+  std::vector<int32_t> asrc((size_t)(N > 0 ? N : 1));
+  dsa_status st = mli_resolve(pattern, N, asrc.data());
+  if (st != DSA_OK) return st;
+  if (!q || !w || !k_cache || !k_scale)
+    return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache and k_scale pointer arrays must not be NULL");
+  if (!sel_buf) return fail(DSA_ERR_INVALID_ARG, "sel_buf must not be NULL");
+  hipStream_t main_s = static_cast<hipStream_t>(stream), side_s = static_cast<hipStream_t>(side_stream);
+  const size_t slot = (size_t)(B > 0 ? B : 0) * (size_t)(topk > 0 ? topk : 0);
+  // the i-th F layer writes slot i of sel_buf
+  std::vector<int> slot_of((size_t)N, -1);
+  for (int l = 0, nf = 0; l < N; ++l)
+    if (pattern[l] == 'F') slot_of[l] = nf++;
+  auto args = [&](int l) {
+    return DecodeArgs{q[l], w[l], k_cache[l], k_scale[l], seq_lens, B, Lmax, H, D, topk,
+                      sel_buf + (size_t)slot_of[l] * slot, nullptr, workspace, workspace_bytes, side_s};
+  };
+  for (int l = 0; l < N; ++l) {
+    if (pattern[l] != 'F') continue;
+    st = validate_decode(args(l));
+    if (st != DSA_OK) {
+      std::string m = g_err;
+      return fail(st, "layer %d: %s", l, m.c_str());
+    }
+  }
+  // Every F layer has a slot of its own, so the indexers never wait for the
+  // attention: after the fork, the only cross-stream edges are "attention of
+  // layer l waits for the indexer that wrote its selection" and the final
+  // join.  Same-device streams need no system-scope fence.
+  EventSet es;
+  hipError_t e = es.create(4, hipEventDisableTiming | hipEventDisableSystemFence);
+  if (e != hipSuccess) return hip_fail(e, "event create");
+  hipEvent_t* written = es.ev;   // ring of two: slot i records written[i & 1]
+  hipEvent_t ev_start = es.ev[2], ev_end = es.ev[3];
+  if ((e = hipEventRecord(ev_start, main_s)) != hipSuccess || (e = hipStreamWaitEvent(side_s, ev_start, 0)) != hipSuccess)
+    return hip_fail(e, "stream fork");
+  int waited = -1;   // slot whose completion `stream` already waits for
+  for (int l = 0; l < N; ++l) {
+    if (pattern[l] == 'F') {
+      st = launch_decode(args(l));
+      if (st != DSA_OK) {
+        std::string m = g_err;
+        return fail(st, "layer %d: %s", l, m.c_str());
+      }
+      if ((e = hipEventRecord(written[slot_of[l] & 1], side_s)) != hipSuccess) return hip_fail(e, "event record");
+    }
+    // written[i & 1] was last recorded by slot i: the attended slot is the
+    // newest or the one before it
+    const int sl = slot_of[asrc[l]];
+    if (sl != waited) {
+      if ((e = hipStreamWaitEvent(main_s, written[sl & 1], 0)) != hipSuccess) return hip_fail(e, "stream wait");
+      waited = sl;
+    }
+    if (attn) attn(l, asrc[l], sel_buf + (size_t)sl * slot, stream, user);
+  }
+  // the main stream continues after the side stream's last work
+  if ((e = hipEventRecord(ev_end, side_s)) != hipSuccess || (e = hipStreamWaitEvent(main_s, ev_end, 0)) != hipSuccess)
+    return hip_fail(e, "stream join");
+  if (attn_src_out) memcpy(attn_src_out, asrc.data(), sizeof(int32_t) * (size_t)N);
+  return ok();
+}
+
+dsa_status standin_sparse_attention_workspace(int B, int topk, size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
+  if (B < 1 || topk < 1 || topk > kMaxTopk) return fail(DSA_ERR_INVALID_ARG, "bad sizes B=%d topk=%d", B, topk);
+  *bytes = (size_t)B * dsa::standin_attn_splits(topk) * dsa::STANDIN_PART * sizeof(float);
+  return ok();
+}
+
+dsa_status standin_sparse_attention(const uint16_t* q, const uint16_t* latent, const int32_t* sel, int B, int Lmax,
+                                    int topk, float scale, float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  size_t need = 0;
+  dsa_status st = standin_sparse_attention_workspace(B, topk, &need);
+  if (st != DSA_OK) return st;
+  if (Lmax < 1) return fail(DSA_ERR_INVALID_ARG, "Lmax must be >= 1");
+  if (!q || !latent || !sel || !out) return fail(DSA_ERR_INVALID_ARG, "q, latent, sel and out must not be NULL");
+  if (!aligned16(q) || !aligned16(latent) || !aligned16(out))
+    return fail(DSA_ERR_INVALID_ARG, "q, latent and out must be 16-byte aligned");
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  dsa::StandinAttnParams p{q, latent, sel, B, Lmax, topk, scale, static_cast<float*>(workspace), out};
+  hipError_t e = dsa::standin_attn_launch(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stand-in attention launch");
   return ok();
 }
 

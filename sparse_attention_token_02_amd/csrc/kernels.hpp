@@ -56,6 +56,28 @@ struct DecodeWsSizes {
   size_t hist_words, bitmap_words, cand_cnt;
 };
 
+// Stand-in sparse attention (one head): latent rows of STANDIN_DK bf16 values,
+// the first STANDIN_DV of which are the value vector.
+constexpr int STANDIN_DK = 576;
+constexpr int STANDIN_DV = 512;
+constexpr int STANDIN_ROWS = 128;             // selection entries per workgroup
+constexpr int STANDIN_PART = 4 + STANDIN_DV;  // floats per partial: max, sum, pad, weighted rows
+
+struct StandinAttnParams {
+  const uint16_t* q;         // [B, STANDIN_DK] bf16
+  const uint16_t* latent;    // [B, Lmax, STANDIN_DK] bf16
+  const int32_t* sel;        // [B, topk], -1 padded
+  int B;
+  int Lmax;
+  int topk;
+  float scale;
+  float* part;               // workspace [B, splits, STANDIN_PART]
+  float* out;                // [B, STANDIN_DV] fp32
+};
+
+int standin_attn_splits(int topk);
+hipError_t standin_attn_launch(const StandinAttnParams& p, hipStream_t stream);
+
 // Largest key index the overlap kernel counts; larger entries are ignored.
 constexpr int OVERLAP_MAX_KEY = (1 << 30) - 1;
 

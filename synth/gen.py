@@ -35,6 +35,7 @@ __all__ = [
     "GAMMA", "mix64_int", "stream_base", "hash_u64", "NORMAL_TABLE", "normal_f32",
     "uniform_int", "bf16_bits", "e4m3_bits", "quant_rows_e4m3", "heavy_positions",
     "STREAM", "CONFIGS", "prefill_inputs", "decode_inputs", "fs_layer_inputs", "fs_decode_layer_inputs",
+    "standin_latent", "standin_query",
     "fs_noise_rows", "decode_lens", "FS_PATTERNS", "ragged_decode_config",
 ]
 
@@ -134,7 +135,7 @@ def quant_rows_e4m3(X) -> tuple[np.ndarray, np.ndarray]:
 # ----------------------------------------------------------------------------
 
 # Stream ids: tensor id * 1024 + layer (the layer is 0 outside the layer-reuse workload).
-STREAM = {"q": 1, "k": 2, "w": 3, "heavy": 4, "lens": 5}
+STREAM = {"q": 1, "k": 2, "w": 3, "heavy": 4, "lens": 5, "latent": 6, "qa": 7}
 
 
 def _sid(name: str, layer: int = 0) -> int:
@@ -310,6 +311,25 @@ def fs_decode_layer_inputs(cfg: dict, layer: int, seqs=None) -> dict:
     q = bf16_bits(fs_noise_rows(cfg, "q", layer, seqs, H * D)).reshape(S, H, D)
     w = bf16_bits((fs_noise_rows(cfg, "w", layer, seqs, H) / _F32(cfg["w_div"])).astype(np.float32))
     return {"cache": cache, "k_scale": kscale, "q": q, "w": w, "lens": decode_lens(cfg)[seqs], "seqs": seqs}
+
+
+def standin_latent(seed: int, which: int, B: int, Lmax: int, seqs=None) -> np.ndarray:
+    """Latent cache number ``which`` for the stand-in attention: bf16 bits
+    [S, Lmax, 576] of N/4, row b*Lmax + s of stream ("latent", which)."""
+    seqs = np.arange(B, dtype=np.int64) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    out = np.empty((len(seqs), Lmax, 576), dtype=np.uint16)
+    for i, b in enumerate(seqs):
+        idx = np.uint64(int(b) * Lmax * 576) + np.arange(Lmax * 576, dtype=np.uint64)
+        X = normal_f32(seed, _sid("latent", which), idx) / _F32(4.0)
+        out[i] = bf16_bits(X.astype(np.float32)).reshape(Lmax, 576)
+    return out
+
+
+def standin_query(seed: int, layer: int, B: int, seqs=None) -> np.ndarray:
+    """Stand-in attention query of layer ``layer``: bf16 bits [S, 576] of N/4."""
+    seqs = np.arange(B, dtype=np.int64) if seqs is None else np.asarray(seqs, dtype=np.int64)
+    idx = seqs[:, None].astype(np.uint64) * np.uint64(576) + np.arange(576, dtype=np.uint64)[None, :]
+    return bf16_bits((normal_f32(seed, _sid("qa", layer), idx) / _F32(4.0)).astype(np.float32))
 
 
 def fs_keys_by_layer(cfg: dict, last_layer: int):

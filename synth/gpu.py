@@ -198,3 +198,15 @@ class DeviceGen:
         w = self.bf16(self.rows_f32(seed, "w", B, H, div=cfg["w_div"], **rs))
         lens = torch.from_numpy(gen.decode_lens(cfg)).to(self.device)
         return {"cache": cache, "k_scale": ks, "q": q, "w": w, "lens": lens}
+
+    def standin_latent(self, seed: int, which: int, B: int, Lmax: int):
+        torch = self.torch
+        out = torch.empty((B, Lmax, 576), dtype=torch.int16, device=self.device)
+        for b in range(B):
+            X = self.rows_f32(seed, "latent", Lmax, 576, row0=b * Lmax, layers=which, rho=0.0, sigma=1.0, div=4.0)
+            out[b] = self.bf16(X)
+            del X
+        return out
+
+    def standin_query(self, seed: int, layer: int, B: int):
+        return self.bf16(self.rows_f32(seed, "qa", B, 576, layers=layer, rho=0.0, sigma=1.0, div=4.0))

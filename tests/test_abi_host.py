@@ -191,6 +191,49 @@ def test_run_decode_layers_rejects_before_any_device_call():
     assert call(qq=arr(FAKE, None, FAKE), cache=arr(FAKE, None, FAKE), wsb=16) == dsa.DSA_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("name", sorted(gen.FS_PATTERNS))
+def test_mli_resolve_matches_schedule_rule(name):
+    import oracle
+    pat = gen.FS_PATTERNS[name]
+    assert dsa.mli_resolve(pat) == oracle.mli_resolve(pat)
+    assert dsa.mli_resolve("FSFFS") == [0, 0, 0, 2, 3]
+    with pytest.raises(dsa.DsaError):
+        dsa.mli_resolve("SFF")
+
+
+def test_run_decode_layers_mli_rejects_before_any_device_call():
+    lib = dsa.lib()
+    P = ctypes.c_void_p * 3
+    full = P(FAKE, FAKE, FAKE)
+    hook = dsa.HOOK_T()
+
+    def call(pattern=b"FSF", N=3, sb=FAKE, wsb=1 << 30, qq=full, H=64):
+        return lib.indexcache_run_decode_layers_mli(pattern, N, qq, full, full, full, FAKE, 2, 1024, H, 128, 16,
+                                                    sb, None, hook, None, FAKE, wsb, None, None)
+    assert call(pattern=b"SFF") == dsa.DSA_ERR_INVALID_ARG
+    assert call(sb=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
+    assert "layer 0" in dsa.dsa_last_error()
+    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(qq=P(FAKE, FAKE, None)) == dsa.DSA_ERR_INVALID_ARG
+    assert "layer 2" in dsa.dsa_last_error()
+
+
+def test_standin_attention_rejects_before_any_device_call():
+    lib = dsa.lib()
+    n = dsa.standin_sparse_attention_workspace(32, 2048)
+    assert n == 32 * 16 * (4 + 512) * 4
+
+    def call(q=FAKE, lat=FAKE, sel=FAKE, B=2, Lmax=100, topk=16, out=FAKE, ws=FAKE, wsb=1 << 20):
+        return lib.standin_sparse_attention(q, lat, sel, B, Lmax, topk, 0.5, out, ws, wsb, None)
+    assert call(sel=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(B=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(topk=5000) == dsa.DSA_ERR_INVALID_ARG
+    assert call(Lmax=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(lat=FAKE + 2) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=64) == dsa.DSA_ERR_WORKSPACE
+
+
 def test_one_hip_runtime_in_process():
     """The library binds to the HIP runtime torch loaded (never a second copy)."""
     import torch  # noqa: F401

@@ -2,13 +2,14 @@
 
 Each mutant replaces one oracle function with a plausible wrong variant (a
 dropped ReLU, a wrong head index, an off-by-one causal prefix, a reversed
-tie rule, ...).  For every mutant at least one pin of
+tie rule, a schedule without the lag, ...).  For every mutant at least one pin of
 ``test_oracle_pins`` has to fail; a mutant that passes all pins would mean
 the pins cannot tell that mistake from the right answer.
 """
 import numpy as np
 import pytest
 
+import oracle
 import oracle.indexer as oi
 from tests import test_oracle_pins as pins
 
@@ -56,6 +57,32 @@ def _no_scale_dequant(codes, scale, fmt):
     return _orig_dequant(codes, None, fmt)
 
 
+_orig_fs_resolve = oi.fs_resolve
+
+
+def _mli_attends_own(pattern):
+    # F layers attend their own selection (IndexCache without the lag)
+    return _orig_fs_resolve(pattern)
+
+
+def _standin_with(values=slice(0, 512), use_scale=True, drop_padding=True):
+    def f(q, latent, sel, scale):
+        q, latent, sel = np.asarray(q), np.asarray(latent), np.asarray(sel)
+        B, Lmax = latent.shape[0], latent.shape[1]
+        out = np.zeros((B, 512))
+        for b in range(B):
+            keep = (sel[b] >= 0) & (sel[b] < Lmax) if drop_padding else (sel[b] < Lmax)
+            rows = sel[b][keep]
+            if len(rows) == 0:
+                continue
+            X = oi.dec_bf16(latent[b, rows])
+            sc = (float(scale) if use_scale else 1.0) * (X @ oi.dec_bf16(q[b]))
+            pr = np.exp(sc - sc.max())
+            out[b] = (pr / pr.sum()) @ X[:, values]
+        return out
+    return f
+
+
 MUTANTS = {
     "no_relu": ("indexer_scores", _scores_with(lambda x, w: x @ w)),
     "abs_instead_of_relu": ("indexer_scores", _scores_with(lambda x, w: np.abs(x) @ w)),
@@ -66,6 +93,10 @@ MUTANTS = {
     "ties_to_higher_index": ("select_topk", _select_with(lambda o, s: np.lexsort((-s, -o)))),
     "keeps_smallest": ("select_topk", _select_with(lambda o, s: np.lexsort((s, o)))),
     "scales_ignored": ("dequant", _no_scale_dequant),
+    "mli_f_layers_attend_own": ("mli_resolve", _mli_attends_own),
+    "standin_scale_ignored": ("standin_attention", _standin_with(use_scale=False)),
+    "standin_values_from_tail": ("standin_attention", _standin_with(values=slice(64, 576))),
+    "standin_padding_read": ("standin_attention", _standin_with(drop_padding=False)),
 }
 
 PINS = [
@@ -79,6 +110,12 @@ PINS = [
     pins.test_single_head_unit_weight_is_relu_gemv,
     pins.test_head_permutation_invariance,
     pins.test_positive_scaling_equivariance,
+    pins.test_mli_resolve_tables,
+    pins.test_mli_run_lags_f_layers,
+    pins.test_hand_example_lagged_schedule,
+    pins.test_standin_attention_zero_query_is_mean_of_values,
+    pins.test_standin_attention_two_rows_weights_three_to_one,
+    pins.test_standin_attention_invariances_and_limits,
 ]
 
 
@@ -86,6 +123,8 @@ PINS = [
 def test_mutant_is_caught(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setattr(oi, attr, fn)
+    if hasattr(oracle, attr):           # the package re-exports the module's functions
+        monkeypatch.setattr(oracle, attr, fn)
     caught = 0
     for pin in PINS:
         try:

@@ -325,6 +325,106 @@ def test_fs_run_reuses_source_output():
     assert outs[1] is outs[0] and outs[2] is outs[0] and outs[4] is outs[3]
 
 
+def test_mli_resolve_tables():
+    """Lagged schedule, written out by hand from its rule: an F layer attends
+    the previous F layer's selection, an S layer the nearest earlier F layer's,
+    the first layer its own."""
+    assert oracle.mli_resolve("F") == [0]
+    assert oracle.mli_resolve("FSFFS") == [0, 0, 0, 2, 3]
+    assert oracle.mli_resolve("FFSSF") == [0, 0, 1, 1, 1]
+    p = gen.FS_PATTERNS
+    assert oracle.mli_resolve(p["all_F"]) == [0] + list(range(46))
+    assert oracle.mli_resolve(p["uniform_1_4"]) == [0] + [4 * ((l - 1) // 4) for l in range(1, 47)]
+    fl = [0, 2, 4, 9, 13, 16, 17, 20, 23, 28, 32, 37]
+    src = oracle.mli_resolve(p["searched_1_4"])
+    assert [src[f] for f in fl] == [0] + fl[:-1]                 # each F layer lags one F layer
+    fs = oracle.fs_resolve(p["searched_1_4"])
+    assert all(src[l] == fs[l] for l in range(47) if l not in fl)  # S layers as in IndexCache
+    for bad in ["SFF", "FXF", ""]:
+        with pytest.raises(ValueError):
+            oracle.mli_resolve(bad)
+
+
+def test_mli_run_lags_f_layers():
+    seen = []
+    outs, asrc, calls = oracle.mli_run("FSFFS", lambda l: (seen.append(l), np.full((2, 2), l))[1])
+    assert seen == [0, 2, 3] and calls == 3 and asrc == [0, 0, 0, 2, 3]
+    assert outs[0] is outs[1] and outs[2] is outs[0] and int(outs[3][0, 0]) == 2 and int(outs[4][0, 0]) == 3
+
+
+def test_hand_example_lagged_schedule():
+    """FSF on the hand example: layer 2 attends layer 0's sets (its own, L2's,
+    differ at t = 3) and layer 0 attends its own."""
+    g = _hand()
+    q = gen.bf16_bits(np.array(g["q"], dtype=np.float32))
+    w = gen.bf16_bits(np.array(g["w"], dtype=np.float32))
+    per_layer = [oracle.prefill(q, None, gen.bf16_bits(np.array(L["k"], dtype=np.float32)), None, w,
+                                "bf16", g["topk"], rows=range(4))["idx"] for L in g["layers"]]
+    outs, asrc, calls = oracle.mli_run(g["fs_pattern"], lambda l: per_layer[l])
+    assert asrc == [0, 0, 0] and calls == 2
+    np.testing.assert_array_equal(outs[2], np.array(g["layers"][0]["idx"]))
+    assert not np.array_equal(outs[2], np.array(g["layers"][2]["idx"]))
+
+
+# ----------------------------------------------------------------------------
+# stand-in attention
+# ----------------------------------------------------------------------------
+
+def _latent(rng, B, Lmax):
+    return gen.bf16_bits((rng.standard_normal((B, Lmax, 576)) / 4).astype(np.float32))
+
+
+def test_standin_attention_zero_query_is_mean_of_values():
+    rng = np.random.default_rng(3)
+    lat = _latent(rng, 2, 50)
+    sel = np.array([[3, 7, 11, -1], [0, 49, -1, -1]])
+    out = oracle.standin_attention(np.zeros((2, 576), dtype=np.uint16), lat, sel, 0.7)
+    for b in range(2):
+        rows = [s for s in sel[b] if s >= 0]
+        want = sum(oracle.dec_bf16(lat[b, s, :512]) for s in rows) / len(rows)
+        np.testing.assert_allclose(out[b], want, rtol=0, atol=1e-15)
+
+
+def test_standin_attention_two_rows_weights_three_to_one():
+    """Scores differing by ln 3 weight the rows 3/4 and 1/4."""
+    rng = np.random.default_rng(4)
+    lat = _latent(rng, 1, 4)
+    lat[0, :, 0] = gen.bf16_bits(np.array([1.0, 0.0, 0.5, 0.5], dtype=np.float32))
+    q = np.zeros((1, 576), dtype=np.uint16)
+    q[0, 0] = gen.bf16_bits(np.array([1.0], dtype=np.float32))[0]
+    out = oracle.standin_attention(q, lat, np.array([[0, 1]]), float(np.log(3.0)))
+    v = oracle.dec_bf16(lat[0, :2, :512])
+    np.testing.assert_allclose(out[0], 0.75 * v[0] + 0.25 * v[1], rtol=0, atol=1e-14)
+
+
+def test_standin_attention_invariances_and_limits():
+    rng = np.random.default_rng(5)
+    B, Lmax = 3, 64
+    lat = _latent(rng, B, Lmax)
+    q = gen.bf16_bits((rng.standard_normal((B, 576)) / 4).astype(np.float32))
+    sel = np.stack([np.sort(rng.choice(Lmax, 8, replace=False)) for _ in range(B)])
+    base = oracle.standin_attention(q, lat, sel, 0.3)
+    # order of the selection does not matter; padding and out-of-range entries are skipped
+    perm = sel[:, ::-1].copy()
+    np.testing.assert_allclose(oracle.standin_attention(q, lat, perm, 0.3), base, rtol=1e-13, atol=1e-15)
+    padded = np.concatenate([sel, np.full((B, 3), -1), np.full((B, 1), Lmax + 5)], axis=1)
+    np.testing.assert_allclose(oracle.standin_attention(q, lat, padded, 0.3), base, rtol=1e-13, atol=1e-15)
+    assert np.all(oracle.standin_attention(q, lat, np.full((B, 4), -1), 0.3) == 0.0)
+    # a dimension on which every latent row agrees shifts all scores equally
+    lat2, q2 = lat.copy(), q.copy()
+    lat2[:, :, 575] = gen.bf16_bits(np.array([2.0], dtype=np.float32))[0]
+    q2[:, 575] = gen.bf16_bits(np.array([3.0], dtype=np.float32))[0]
+    lat_ref = lat.copy()
+    lat_ref[:, :, 575] = 0
+    np.testing.assert_allclose(oracle.standin_attention(q2, lat2, sel, 0.3),
+                               oracle.standin_attention(q, lat_ref, sel, 0.3), rtol=1e-12, atol=1e-14)
+    # a very large scale picks the value of the highest-scoring row
+    hard = oracle.standin_attention(q, lat, sel, 1e4)
+    for b in range(B):
+        d = [float(oracle.dec_bf16(lat[b, s]) @ oracle.dec_bf16(q[b])) for s in sel[b]]
+        np.testing.assert_allclose(hard[b], oracle.dec_bf16(lat[b, sel[b][int(np.argmax(d))], :512]), atol=1e-12)
+
+
 # ----------------------------------------------------------------------------
 # overlap
 # ----------------------------------------------------------------------------
