@@ -302,6 +302,15 @@ def run_fs(args, g, dsa, gen, stream):
         if s_layers:
             res.setdefault("s_layer_mean_overlap_with_source", {})[pname] = round(
                 float(sum(ratio[l, src[l]] for l in s_layers) / len(s_layers)), 4)
+    # greedy search at retention 1/4 with the overlap proxy as its loss: a
+    # labelled baseline (the pages' search uses a calibration LM loss, which
+    # needs a trained model)
+    proxy = lambda p: dsa.indexcache_overlap_proxy_loss(p, ratio)
+    t0 = time.perf_counter()
+    pat, trace, flipped = dsa.indexcache_greedy_search(N, N - 12, proxy)
+    res["proxy_greedy_1_4"] = {"loss": "overlap proxy (baseline only)", "pattern": pat,
+                               "proxy_loss": round(trace[-1], 5), "search_ms": round((time.perf_counter() - t0) * 1e3, 1),
+                               "proxy_loss_of": {p: round(proxy(v), 5) for p, v in gen.FS_PATTERNS.items()}}
     return res
 
 

@@ -194,6 +194,41 @@ dsa_status indexcache_run_decode_layers(const char* pattern, int N,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Training-free pattern search.  [IC] 3.1 (greedy layer selection): start
+ * from all F; at every step try turning each remaining F layer into S,
+ * score each trial with a calibration loss and commit the lowest; K steps
+ * (K = 3N/4 for retention 1/4).  [IC] 5.2: a full run costs N(N-1)/2
+ * evaluations, and similarity proxies do not predict the loss.
+ * ------------------------------------------------------------------------ */
+
+/* Loss of a pattern (N characters, NUL-terminated), e.g. a model's LM loss on
+ * calibration data; the caller owns what it runs.  NaN is an error. */
+typedef double (*indexcache_loss_fn)(const char* pattern, int N, void* user);
+
+/*
+ * Host only, no device work (the loss may do any).  Runs `steps` greedy
+ * steps from all F (0 <= steps <= N-1; the first layer is never turned into
+ * S).  Among trials with equal loss the lowest layer wins.
+ * pattern_out  host char[N + 1]: the final pattern, NUL-terminated
+ * loss_trace   host double[steps + 1] or NULL: the all-F loss, then the loss
+ *              committed at every step
+ * flipped      host int32[steps] or NULL: the layer turned into S at every step
+ * The loss is called 1 + sum_{i<steps} (N-1-i) times, in layer order within
+ * a step.
+ */
+dsa_status indexcache_greedy_search(int N, int steps, indexcache_loss_fn loss, void* user,
+                                    char* pattern_out, double* loss_trace, int32_t* flipped);
+
+/*
+ * A similarity proxy for the loss, as a labelled baseline only ([IC] 5.2
+ * reports that such proxies fail): the mean over all N layers of
+ * 1 - ratio[l][src(l)] over the S layers, with ratio the N x N host overlap
+ * ratio matrix of an all-F run (topk_overlap_matrix) and src the pattern's
+ * source layers.  Host only.
+ */
+dsa_status indexcache_overlap_proxy_loss(const char* pattern, int N, const double* ratio, double* loss);
+
+/* ------------------------------------------------------------------------
  * Multi-layer Indexer (lagged) decode schedule.  [ML] abstract: adjacent
  * layers select nearly the same tokens, so a layer attends the selection of
  * the previous indexer layer instead of its own; its own indexer then runs

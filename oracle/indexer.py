@@ -16,6 +16,11 @@ Sources (the pages are cited by title and section):
   cached index tensor, Shared (S) layers skip it and use the indices of the
   nearest earlier F layer, f(l) = max{j < l : c_j = F}; the first layer is
   always F.
+* Same report, section 3.1: the training-free route chooses the pattern
+  greedily -- from all F, each step tries turning every remaining F layer
+  into S, evaluates a calibration loss for each trial and commits the best,
+  for K steps; section 5.2: a full run costs N(N-1)/2 evaluations and
+  similarity proxies do not predict the loss.
 * Multi-layer Indexer abstract (equalang.com): at decode the indexer scores
   the whole cache of the sequence and keeps the k = 2048 highest.  Adjacent
   layers select nearly the same tokens, so in the lagged schedule a layer
@@ -43,7 +48,8 @@ import numpy as np
 
 __all__ = [
     "dec_e4m3", "dec_bf16", "dequant", "indexer_scores", "select_topk",
-    "prefill", "decode", "fs_resolve", "fs_run", "mli_resolve", "mli_run", "standin_attention",
+    "prefill", "decode", "fs_resolve", "fs_run", "fs_greedy_search", "overlap_proxy_loss",
+    "mli_resolve", "mli_run", "standin_attention",
     "overlap_counts", "overlap_ratio",
 ]
 
@@ -223,6 +229,38 @@ def fs_run(pattern: str, layer_topk):
             calls += 1
         outs.append(cache)
     return outs, src, calls
+
+
+def fs_greedy_search(N: int, steps: int, loss):
+    """Greedy pattern search: start from all F; at every step turn into S the
+    F layer (never the first) whose trial pattern has the lowest
+    ``loss(pattern)``, the lowest layer winning ties.  Returns (pattern, the
+    all-F loss then the committed loss per step, the layer flipped per step)."""
+    if not (0 <= steps <= N - 1):
+        raise ValueError("steps must be in [0, N-1]")
+    pat = ["F"] * N
+    trace = [float(loss("".join(pat)))]
+    flipped = []
+    for _ in range(steps):
+        trials = []
+        for l in range(1, N):
+            if pat[l] == "F":
+                trial = pat.copy()
+                trial[l] = "S"
+                trials.append((float(loss("".join(trial))), l))
+        best = min(trials)          # lowest loss, then lowest layer
+        pat[best[1]] = "S"
+        trace.append(best[0])
+        flipped.append(best[1])
+    return "".join(pat), trace, flipped
+
+
+def overlap_proxy_loss(pattern: str, ratio) -> float:
+    """Similarity proxy (a baseline the report says fails): the lost overlap
+    1 - ratio[l, src(l)] summed over the S layers, divided by the layer count."""
+    src = fs_resolve(pattern)
+    r = np.asarray(ratio, dtype=np.float64)
+    return sum(1.0 - r[l, src[l]] for l, c in enumerate(pattern) if c == "S") / len(pattern)
 
 
 def mli_resolve(pattern: str) -> list[int]:

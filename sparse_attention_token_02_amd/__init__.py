@@ -29,7 +29,8 @@ EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
     "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill",
     "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode",
-    "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers", "mli_resolve",
+    "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers",
+    "indexcache_greedy_search", "indexcache_overlap_proxy_loss", "mli_resolve",
     "indexcache_run_decode_layers_mli", "standin_sparse_attention_workspace", "standin_sparse_attention",
     "topk_overlap_matrix",
 )
@@ -41,6 +42,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
 HOOK_T = ctypes.CFUNCTYPE(None, _i32, _i32, _vp, _vp, _vp)
+LOSS_T = ctypes.CFUNCTYPE(ctypes.c_double, ctypes.c_char_p, _i32, _vp)
 
 _lib.dsa_last_error.restype = ctypes.c_char_p
 _lib.dsa_last_error.argtypes = []
@@ -68,6 +70,12 @@ _lib.indexcache_run_decode_layers.argtypes = [ctypes.c_char_p, _i32, ctypes.POIN
                                               ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, _i32, _i32, _i32,
                                               _i32, _i32, _vp, ctypes.POINTER(ctypes.c_int32), HOOK_T, _vp, _vp,
                                               _sz, _vp]
+_lib.indexcache_greedy_search.restype = _i32
+_lib.indexcache_greedy_search.argtypes = [_i32, _i32, LOSS_T, _vp, ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int32)]
+_lib.indexcache_overlap_proxy_loss.restype = _i32
+_lib.indexcache_overlap_proxy_loss.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(ctypes.c_double),
+                                               ctypes.POINTER(ctypes.c_double)]
 _lib.mli_resolve.restype = _i32
 _lib.mli_resolve.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(ctypes.c_int32)]
 _lib.indexcache_run_decode_layers_mli.restype = _i32
@@ -274,6 +282,41 @@ def indexcache_run_decode_layers(pattern: str, q, w, k_cache, k_scale, seq_lens,
     if errors:
         raise errors[0]
     return tcache, list(src[:N])
+
+
+def indexcache_greedy_search(N: int, steps: int, loss):
+    """Greedy F/S search from all F: ``loss(pattern: str) -> float`` is called
+    for the all-F pattern and for every trial.  Returns (pattern, loss trace
+    [steps + 1], flipped layer per step)."""
+    import math
+    out = ctypes.create_string_buffer(N + 1)
+    trace = (ctypes.c_double * (steps + 1))()
+    flipped = (ctypes.c_int32 * max(steps, 1))()
+    errors = []
+
+    def _loss(pat, n, user):
+        try:
+            return float(loss(pat.decode()))
+        except Exception as e:  # surfaced after the call returns
+            errors.append(e)
+            return math.nan
+
+    rc = _lib.indexcache_greedy_search(N, steps, LOSS_T(_loss), None, out, trace, flipped)
+    if errors:
+        raise errors[0]
+    _check(rc)
+    return out.value.decode(), list(trace), list(flipped[:steps])
+
+
+def indexcache_overlap_proxy_loss(pattern: str, ratio) -> float:
+    """Overlap-proxy loss of a pattern (a labelled baseline), ratio: [N, N]
+    host float64 overlap ratios of an all-F run."""
+    import numpy as np
+    r = np.ascontiguousarray(ratio, dtype=np.float64)
+    v = ctypes.c_double(0.0)
+    _check(_lib.indexcache_overlap_proxy_loss(pattern.encode(), len(pattern),
+                                              r.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), ctypes.byref(v)))
+    return v.value
 
 
 def mli_resolve(pattern: str) -> list[int]:

@@ -33,7 +33,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 def _compile(src: str, obj_dir: str, extra: list[str]) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    # the host-only C-ABI layer checks caller values (a loss callback) for NaN
+    host_only = ["-fhonor-nans"] if src == "abi.cpp" else []
+    cmd = [HIPCC, *COMMON, *host_only, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -401,6 +402,49 @@ dsa_status indexcache_run_decode_layers(const char* pattern, int N, const uint16
     if (hook) hook(l, src[l], tcache, stream, user);
   }
   if (src_layer_out) memcpy(src_layer_out, src.data(), sizeof(int32_t) * (size_t)N);
+  return ok();
+}
+
+dsa_status indexcache_greedy_search(int N, int steps, indexcache_loss_fn loss, void* user, char* pattern_out,
+                                    double* loss_trace, int32_t* flipped) {
+  if (N < 1) return fail(DSA_ERR_INVALID_ARG, "N must be >= 1 (got %d)", N);
+  if (steps < 0 || steps > N - 1) return fail(DSA_ERR_INVALID_ARG, "steps must be in [0, N-1] (got %d)", steps);
+  if (!loss || !pattern_out) return fail(DSA_ERR_INVALID_ARG, "loss and pattern_out must not be NULL");
+  std::string pat((size_t)N, 'F');
+  double cur = loss(pat.c_str(), N, user);
+  if (std::isnan(cur)) return fail(DSA_ERR_INVALID_ARG, "loss returned NaN for the all-F pattern");
+  if (loss_trace) loss_trace[0] = cur;
+  for (int step = 0; step < steps; ++step) {
+    int best_l = -1;
+    double best = 0.0;
+    for (int l = 1; l < N; ++l) {   // the first layer stays F
+      if (pat[(size_t)l] != 'F') continue;
+      pat[(size_t)l] = 'S';
+      const double v = loss(pat.c_str(), N, user);
+      pat[(size_t)l] = 'F';
+      if (std::isnan(v)) return fail(DSA_ERR_INVALID_ARG, "loss returned NaN at step %d, layer %d", step, l);
+      if (best_l < 0 || v < best) {   // strict: the lowest layer wins a tie
+        best_l = l;
+        best = v;
+      }
+    }
+    pat[(size_t)best_l] = 'S';
+    if (loss_trace) loss_trace[step + 1] = best;
+    if (flipped) flipped[step] = best_l;
+  }
+  memcpy(pattern_out, pat.c_str(), (size_t)N + 1);
+  return ok();
+}
+
+dsa_status indexcache_overlap_proxy_loss(const char* pattern, int N, const double* ratio, double* loss) {
+  if (!ratio || !loss) return fail(DSA_ERR_INVALID_ARG, "ratio and loss must not be NULL");
+  std::vector<int32_t> src((size_t)(N > 0 ? N : 1));
+  dsa_status st = indexcache_resolve(pattern, N, src.data());
+  if (st != DSA_OK) return st;
+  double lost = 0.0;
+  for (int l = 0; l < N; ++l)
+    if (pattern[l] == 'S') lost += 1.0 - ratio[(size_t)l * N + src[l]];
+  *loss = lost / N;
   return ok();
 }
 

@@ -234,6 +234,44 @@ def test_standin_attention_rejects_before_any_device_call():
     assert call(wsb=64) == dsa.DSA_ERR_WORKSPACE
 
 
+def test_greedy_search_matches_oracle():
+    """The library's search against the oracle's, on seeded table losses
+    (a hash of the pattern) and on the overlap proxy of a random matrix."""
+    import hashlib
+    import numpy as np
+    import oracle
+    for N, steps in [(1, 0), (2, 1), (9, 6), (20, 15)]:
+        loss = lambda p: int(hashlib.sha256(p.encode()).hexdigest()[:6], 16) / 2.0 ** 24
+        assert dsa.indexcache_greedy_search(N, steps, loss) == oracle.fs_greedy_search(N, steps, loss)
+    rng = np.random.default_rng(2)
+    R = rng.random((12, 12))
+    R = (R + R.T) / 2
+    np.fill_diagonal(R, 1.0)
+    for p in ["F" * 12, "FSFSFSFSFSFS", "FSSSSSSSSSSF"]:
+        assert dsa.indexcache_overlap_proxy_loss(p, R) == pytest.approx(oracle.overlap_proxy_loss(p, R), abs=1e-15)
+    proxy = lambda p: dsa.indexcache_overlap_proxy_loss(p, R)
+    assert dsa.indexcache_greedy_search(12, 9, proxy) == oracle.fs_greedy_search(12, 9, proxy)
+
+
+def test_greedy_search_rejects_and_reports_loss_errors():
+    with pytest.raises(dsa.DsaError):
+        dsa.indexcache_greedy_search(5, 5, lambda p: 0.0)
+    with pytest.raises(dsa.DsaError):
+        dsa.indexcache_greedy_search(0, 0, lambda p: 0.0)
+    with pytest.raises(dsa.DsaError):
+        dsa.indexcache_greedy_search(4, 2, lambda p: float("nan"))
+
+    class Boom(Exception):
+        pass
+
+    def bad(p):
+        raise Boom(p)
+    with pytest.raises(Boom):
+        dsa.indexcache_greedy_search(4, 2, bad)
+    with pytest.raises(dsa.DsaError):
+        dsa.indexcache_overlap_proxy_loss("SFF", [[1.0] * 3] * 3)
+
+
 def test_one_hip_runtime_in_process():
     """The library binds to the HIP runtime torch loaded (never a second copy)."""
     import torch  # noqa: F401

@@ -58,6 +58,18 @@ def _no_scale_dequant(codes, scale, fmt):
 
 
 _orig_fs_resolve = oi.fs_resolve
+_orig_greedy = oi.fs_greedy_search
+
+
+def _greedy_ties_high(N, steps, loss):
+    # a tie goes to the highest layer: search the layers in reverse order
+    return _orig_greedy(N, steps, lambda p: loss(p) - 1e-12 * p.rfind("S"))
+
+
+def _proxy_counts_f_layers(pattern, ratio):
+    src = oi.fs_resolve(pattern)
+    r = np.asarray(ratio, dtype=np.float64)
+    return sum(1.0 - r[l, src[l] - 1 if l else 0] for l in range(len(pattern))) / len(pattern)
 
 
 def _mli_attends_own(pattern):
@@ -94,6 +106,8 @@ MUTANTS = {
     "keeps_smallest": ("select_topk", _select_with(lambda o, s: np.lexsort((s, o)))),
     "scales_ignored": ("dequant", _no_scale_dequant),
     "mli_f_layers_attend_own": ("mli_resolve", _mli_attends_own),
+    "greedy_ties_to_highest_layer": ("fs_greedy_search", _greedy_ties_high),
+    "proxy_wrong_source": ("overlap_proxy_loss", _proxy_counts_f_layers),
     "standin_scale_ignored": ("standin_attention", _standin_with(use_scale=False)),
     "standin_values_from_tail": ("standin_attention", _standin_with(values=slice(64, 576))),
     "standin_padding_read": ("standin_attention", _standin_with(drop_padding=False)),
@@ -110,6 +124,9 @@ PINS = [
     pins.test_single_head_unit_weight_is_relu_gemv,
     pins.test_head_permutation_invariance,
     pins.test_positive_scaling_equivariance,
+    pins.test_greedy_search_additive_loss_closed_form,
+    pins.test_greedy_search_ties_and_hand_traced_interaction,
+    pins.test_overlap_proxy_closed_form,
     pins.test_mli_resolve_tables,
     pins.test_mli_run_lags_f_layers,
     pins.test_hand_example_lagged_schedule,

@@ -325,6 +325,53 @@ def test_fs_run_reuses_source_output():
     assert outs[1] is outs[0] and outs[2] is outs[0] and outs[4] is outs[3]
 
 
+def test_greedy_search_additive_loss_closed_form():
+    """With loss = sum of a fixed cost per S layer, the greedy search turns
+    layers into S in increasing cost order (the first layer never)."""
+    rng = np.random.default_rng(8)
+    N = 12
+    cost = rng.permutation(N).astype(float) + 0.5
+    loss = lambda p: sum(cost[l] for l, c in enumerate(p) if c == "S")
+    pat, trace, flipped = oracle.fs_greedy_search(N, N - 1, loss)
+    order = [int(l) for l in np.argsort(cost) if l != 0]
+    assert flipped == order and pat == "F" + "S" * (N - 1)
+    assert trace == [0.0] + list(np.cumsum([cost[l] for l in order]))
+    pat9, _, _ = oracle.fs_greedy_search(N, 9, loss)
+    assert pat9.count("F") == 3 and pat9[0] == "F"
+
+
+def test_greedy_search_evaluation_count_matches_report():
+    """A full run (N-1 steps) evaluates N(N-1)/2 trial patterns, the count the
+    deep-dive report gives for the full greedy search, plus the all-F start."""
+    for N in (2, 5, 47):
+        seen = []
+        oracle.fs_greedy_search(N, N - 1, lambda p: (seen.append(p), 0.0)[1])
+        assert len(seen) == 1 + N * (N - 1) // 2
+        assert seen[0] == "F" * N and all(p[0] == "F" for p in seen)
+
+
+def test_greedy_search_ties_and_hand_traced_interaction():
+    # a constant loss: every tie goes to the lowest layer
+    assert oracle.fs_greedy_search(6, 4, lambda p: 1.0)[2] == [1, 2, 3, 4]
+    # a hand-made table where the greedy first step blocks the best pair:
+    # FSFF is the best single flip, but FFSS is the best pair
+    table = {"FFFF": 0.0, "FSFF": 1.0, "FFSF": 2.0, "FFFS": 2.0, "FSSF": 5.0, "FSFS": 5.0, "FFSS": 1.5,
+             "FSSS": 9.0}
+    pat, trace, flipped = oracle.fs_greedy_search(4, 2, lambda p: table[p])
+    assert (pat, trace, flipped) == ("FSSF", [0.0, 1.0, 5.0], [1, 2])
+    with pytest.raises(ValueError):
+        oracle.fs_greedy_search(4, 4, lambda p: 0.0)
+
+
+def test_overlap_proxy_closed_form():
+    R = np.array([[1.0, 0.8, 0.5, 0.4], [0.8, 1.0, 0.7, 0.6], [0.5, 0.7, 1.0, 0.9], [0.4, 0.6, 0.9, 1.0]])
+    assert oracle.overlap_proxy_loss("FFFF", R) == 0.0
+    # FSFS: layer 1 reuses 0 (lost 0.2), layer 3 reuses 2 (lost 0.1)
+    assert abs(oracle.overlap_proxy_loss("FSFS", R) - 0.3 / 4) < 1e-15
+    # FSSS: layers 1, 2, 3 all reuse 0: lost 0.2 + 0.5 + 0.6
+    assert abs(oracle.overlap_proxy_loss("FSSS", R) - 1.3 / 4) < 1e-15
+
+
 def test_mli_resolve_tables():
     """Lagged schedule, written out by hand from its rule: an F layer attends
     the previous F layer's selection, an S layer the nearest earlier F layer's,
