@@ -11,7 +11,8 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|fs_47|fs_decode_47|mli_decode_47``) print their own line.
+(``--workload tiny|prefill_196k|prefill_32k_chunked|fs_47|fs_decode_47|mli_decode_47``)
+print their own line.
 """
 from __future__ import annotations
 
@@ -247,6 +248,8 @@ def run_workload(args):
                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                              "frac": round(tf / peak, 4), "traffic": None},
                 "config": {"workload": name, **{k: v for k, v in cfg.items() if k != "kind"}}}
+    if name == "prefill_32k_chunked":
+        return run_prefill_chunked(args, g, dsa, gen, stream)
     if name == "fs_47":
         return run_fs(args, g, dsa, gen, stream)
     if name == "fs_decode_47":
@@ -254,6 +257,34 @@ def run_workload(args):
     if name == "mli_decode_47":
         return run_mli_decode(args, g, dsa, gen, stream)
     raise SystemExit(f"unknown workload {name}")
+
+
+def run_prefill_chunked(args, g, dsa, gen, stream):
+    """The L=32768 prefill fed as four chunks of 8192 query rows in order
+    (each chunk against all keys so far), as a serving engine feeds a long
+    prompt; the same causal pairs as one whole-sequence call."""
+    import torch
+    cfg = gen.CONFIGS["prefill_32k"]
+    L, H, D, topk = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
+    C = 8192
+    dev = g.device
+    p = g.prefill_inputs(cfg)
+    out = torch.empty((L, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_indexer_topk_prefill_workspace(C, H, D, topk, "fp8"), dtype=torch.uint8, device=dev)
+
+    def chunks():
+        for q0 in range(0, L, C):
+            dsa.dsa_indexer_topk_prefill_chunk(p["q"][q0:q0 + C], p["q_scale"][q0:q0 + C], p["k"][:q0 + C],
+                                               p["k_scale"][:q0 + C], p["w"][q0:q0 + C], q0, topk, "fp8",
+                                               out_idx=out[q0:q0 + C], workspace=ws, stream=stream)
+    ms = time_calls(chunks, args.steps, args.warmup, stream)
+    avg = sum(ms) / len(ms)
+    tf = prefill_flops(L, H, D) / (avg * 1e-3) / 1e12
+    return {"metric": METRIC, "workload": "prefill_32k_chunked", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_sequence": round(avg, 4), "chunk_rows": C,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+            "config": {"workload": "prefill_32k_chunked", "L": L, "H": H, "D": D, "topk": topk, "chunk": C}}
 
 
 def run_fs(args, g, dsa, gen, stream):

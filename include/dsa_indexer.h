@@ -107,6 +107,27 @@ dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t
                                     int32_t* out_idx, float* out_topk_score, float* out_dense_score,
                                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Chunked prefill: a block of Lq query rows at absolute positions
+ * q_offset .. q_offset + Lq - 1 of one sequence, against that sequence's
+ * keys 0 .. q_offset + Lq - 1 (the keys of earlier chunks already in the
+ * cache, then the chunk's own).  Row i of the block scores keys
+ * 0 .. q_offset + i, as row q_offset + i of a whole-sequence prefill would,
+ * and gets the same selection ([IS] 2: the indexer and top-k run per layer
+ * over everything before the query; serving engines feed long prompts in
+ * such chunks).
+ * q [Lq, H, D], q_scale ([Lq] or [Lq, H]), w [Lq, H]: the block's rows;
+ * k [q_offset + Lq, D], k_scale [q_offset + Lq]: all keys so far;
+ * out_idx / out_topk_score [Lq, topk].  q_offset >= 0, Lq >= 1; other
+ * arguments and limits as for dsa_indexer_topk_prefill (no dense output).
+ * The workspace is dsa_indexer_topk_prefill_workspace(Lq, H, D, topk, dt).
+ */
+dsa_status dsa_indexer_topk_prefill_chunk(const void* q, const float* q_scale, int64_t q_scale_head_stride,
+                                          const void* k, const float* k_scale, const uint16_t* w,
+                                          int q_offset, int Lq, int H, int D, int topk, dsa_dtype dt,
+                                          int32_t* out_idx, float* out_topk_score,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Decode: B sequences with one new query each, at position len_b - 1, whose
  * own key is already in the cache; the query scores the whole cache

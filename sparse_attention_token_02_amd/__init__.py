@@ -27,7 +27,7 @@ DSA_BF16, DSA_FP8_E4M3 = 0, 1
 
 EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
-    "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill",
+    "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill", "dsa_indexer_topk_prefill_chunk",
     "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode",
     "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers",
     "indexcache_greedy_search", "indexcache_overlap_proxy_loss", "mli_resolve",
@@ -53,6 +53,9 @@ _lib.dsa_indexer_topk_prefill_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32
 _lib.dsa_indexer_topk_prefill.restype = _i32
 _lib.dsa_indexer_topk_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.dsa_indexer_topk_prefill_chunk.restype = _i32
+_lib.dsa_indexer_topk_prefill_chunk.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_indexer_topk_decode_workspace.restype = _i32
 _lib.dsa_indexer_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 _lib.dsa_indexer_topk_decode.restype = _i32
@@ -174,6 +177,28 @@ def dsa_indexer_topk_prefill(q, q_scale, k, k_scale, w, topk: int, dt, *, q_scal
         _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), L, H, D, topk, _dt(dt),
         _ptr(out_idx), _ptr(out_topk_score), _ptr(out_dense_score), _ptr(ws), ws.numel(), _stream(stream)))
     return out_idx, out_topk_score, out_dense_score
+
+
+def dsa_indexer_topk_prefill_chunk(q, q_scale, k, k_scale, w, q_offset: int, topk: int, dt, *,
+                                   q_scale_head_stride: int = 0, out_idx=None, out_topk_score=None,
+                                   want_scores: bool = False, workspace=None, stream=None):
+    """A block of query rows at positions q_offset .. q_offset+Lq-1: q [Lq,H,D],
+    w [Lq,H], q_scale [Lq] or [Lq,H] or None; k [q_offset+Lq, D], k_scale
+    [q_offset+Lq] or None.  Returns (idx [Lq,topk] int32, topk scores or None)."""
+    import torch
+    Lq, H, D = q.shape
+    dev = q.device
+    if k.shape[0] != q_offset + Lq:
+        raise ValueError(f"k must hold q_offset + Lq = {q_offset + Lq} keys (has {k.shape[0]})")
+    if out_idx is None:
+        out_idx = torch.empty((Lq, topk), dtype=torch.int32, device=dev)
+    if out_topk_score is None and want_scores:
+        out_topk_score = torch.empty((Lq, topk), dtype=torch.float32, device=dev)
+    ws = _workspace(dsa_indexer_topk_prefill_workspace(Lq, H, D, topk, dt), dev, workspace)
+    _check(_lib.dsa_indexer_topk_prefill_chunk(
+        _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), q_offset, Lq, H, D, topk,
+        _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_topk_score
 
 
 def dsa_indexer_topk_decode_workspace(B: int, Lmax: int, H: int, D: int, topk: int) -> int:

@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cmath>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -87,7 +88,7 @@ struct PrefillArgs {
   const void* k;
   const float* k_scale;
   const uint16_t* w;
-  int L, H, D, topk;
+  int L, H, D, topk;           // L: query rows
   dsa_dtype dt;
   int32_t* out_idx;
   float* out_score;
@@ -95,6 +96,7 @@ struct PrefillArgs {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  int q0 = 0;                  // absolute position of query row 0; keys are q0 + L
 };
 
 dsa_status validate_prefill(const PrefillArgs& a, bool check_dense = true) {
@@ -124,7 +126,8 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   p.k = static_cast<const uint8_t*>(a.k);
   p.k_scale = a.k_scale;
   p.w = a.w;
-  p.L = a.L;
+  p.L = a.q0 + a.L;
+  p.q0 = a.q0;
   p.topk = a.topk;
   p.cap = prefill_cap((int)a.dt, a.H, a.D, a.topk);
   p.sample_m = dsa::prefill_sample_keys((int)a.dt, a.H, a.D);
@@ -276,6 +279,24 @@ dsa_status dsa_indexer_topk_prefill(const void* q, const float* q_scale, int64_t
   PrefillArgs a{q, q_scale, q_scale_head_stride, k, k_scale, w, L, H, D, topk, dt, out_idx,
                 out_topk_score, out_dense_score, workspace, workspace_bytes,
                 static_cast<hipStream_t>(stream)};
+  dsa_status st = validate_prefill(a);
+  if (st != DSA_OK) return st;
+  st = launch_prefill(a);
+  if (st != DSA_OK) return st;
+  return ok();
+}
+
+dsa_status dsa_indexer_topk_prefill_chunk(const void* q, const float* q_scale, int64_t q_scale_head_stride,
+                                          const void* k, const float* k_scale, const uint16_t* w, int q_offset,
+                                          int Lq, int H, int D, int topk, dsa_dtype dt, int32_t* out_idx,
+                                          float* out_topk_score, void* workspace, size_t workspace_bytes,
+                                          void* stream) {
+  if (q_offset < 0) return fail(DSA_ERR_INVALID_ARG, "q_offset must be >= 0 (got %d)", q_offset);
+  if (Lq >= 1 && q_offset > INT32_MAX - Lq)
+    return fail(DSA_ERR_INVALID_ARG, "q_offset + Lq must fit in int32");
+  PrefillArgs a{q, q_scale, q_scale_head_stride, k, k_scale, w, Lq, H, D, topk, dt, out_idx,
+                out_topk_score, nullptr, workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  a.q0 = q_offset;
   dsa_status st = validate_prefill(a);
   if (st != DSA_OK) return st;
   st = launch_prefill(a);

@@ -11,24 +11,25 @@ namespace dsa {
 constexpr int OVERLAP_MAX_N = 64;
 
 struct PrefillParams {
-  const uint8_t* q;          // [L, H, D] e4m3 codes or bf16 (as bytes)
+  const uint8_t* q;          // [L - q0, H, D] e4m3 codes or bf16 (as bytes)
   const float* q_scale;      // nullable; element (t, h) at t*qs_row + h*qs_head
   int64_t qs_row;
   int64_t qs_head;
   const uint8_t* k;          // [L, D]
   const float* k_scale;      // [L], nullable
   const uint16_t* w;         // [L, H] bf16
-  int L;
+  int L;                     // keys (query rows are the absolute positions q0 .. L-1)
+  int q0;                    // absolute position of query row 0 (0 for a whole sequence)
   int topk;
   int cap;                   // candidate list capacity per row
   int sample_m;              // keys per row in the threshold sample (0: no sample)
-  int32_t* out_idx;          // [L, topk]
-  float* out_score;          // [L, topk], nullable
-  float* out_dense;          // [L, L], nullable
+  int32_t* out_idx;          // [L - q0, topk]
+  float* out_score;          // [L - q0, topk], nullable
+  float* out_dense;          // [L - q0, L], nullable
   float* ws_sc;              // [grid, rows_per_item, cap]
   int32_t* ws_ix;            // [grid, rows_per_item, cap]
   int* counter;              // work counter
-  int n_items;               // ceil(L / rows_per_item)
+  int n_items;               // ceil((L - q0) / rows_per_item)
 };
 
 struct DecodeParams {

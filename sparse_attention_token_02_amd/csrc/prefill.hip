@@ -174,7 +174,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     __syncthreads();
     const int item = sh.item;
     if (item >= p.n_items) break;
-    const int t0 = (p.n_items - 1 - item) * C::RW;
+    const int t0 = p.q0 + (p.n_items - 1 - item) * C::RW;
     const int kend = min(t0 + C::RW, L);
     const int ntiles = (kend + C::TK - 1) / C::TK;
 
@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           if (t < L) {
-            const uint8_t* src = p.q + ((size_t)t * H + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
+            const uint8_t* src = p.q + ((size_t)(t - p.q0) * H + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
             qa[mb][ks] = load_opnd<C::FP8>(src);
           } else {
             qa[mb][ks] = zero_opnd<C::FP8>();
@@ -202,8 +202,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       const int t = t0 + i / H, head = i % H;
       float v = 0.f;
       if (t < L) {
-        v = bf16_to_f32(p.w[(size_t)t * H + head]);
-        if (p.q_scale) v *= p.q_scale[(size_t)t * p.qs_row + (size_t)head * p.qs_head];
+        v = bf16_to_f32(p.w[(size_t)(t - p.q0) * H + head]);
+        if (p.q_scale) v *= p.q_scale[(size_t)(t - p.q0) * p.qs_row + (size_t)head * p.qs_head];
       }
       sh.weff[i] = v;
     }
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
             tile_scores(tile, ksc_t, [&](int pair, float score) {
               const int s = kt + 64 * pair + lane;
               if constexpr (DENSE) {
-                if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)tr * L + s] = s <= tr ? score : -__builtin_inff();
+                if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)(tr - p.q0) * L + s] = s <= tr ? score : -__builtin_inff();
               }
               const bool pass = (s <= tr) && (score > thr[0]);
               const uint64_t m = ballot64(pass);
@@ -483,7 +483,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
                 const float score = sc[r];
                 const int tr = t0 + row_base + r;
                 if constexpr (DENSE) {
-                  if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)tr * L + s] = s <= tr ? score : -__builtin_inff();
+                  if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)(tr - p.q0) * L + s] = s <= tr ? score : -__builtin_inff();
                 }
                 const bool pass = (s <= tr) && (score > thr[r]);
                 const uint64_t m = ballot64(pass);
@@ -589,8 +589,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int row = wave * C::QPW + rr;
         const int t = t0 + row;
         if (t >= L) continue;
-        int* dix = p.out_idx + (size_t)t * p.topk;
-        float* dsc = p.out_score ? p.out_score + (size_t)t * p.topk : nullptr;
+        int* dix = p.out_idx + (size_t)(t - p.q0) * p.topk;
+        float* dsc = p.out_score ? p.out_score + (size_t)(t - p.q0) * p.topk : nullptr;
         wave_select<true>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix,
                           p.topk, sh.whist[wave], nullptr, lbuf, lcap);
       }
@@ -690,7 +690,7 @@ int prefill_list_capacity(int dt, int H, int D, int topk) {
 }
 
 hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream) {
-  const long long n_dense = p.out_dense ? (long long)p.L * p.L : 0;
+  const long long n_dense = p.out_dense ? (long long)(p.L - p.q0) * p.L : 0;
   const int pg = n_dense ? 1024 : 1;
   hipLaunchKernelGGL(prefill_prepare_kernel, dim3(pg), dim3(256), 0, stream, p.counter, p.out_dense, n_dense);
 #define DSA_PF_CASE(DT_, H_, D_) \

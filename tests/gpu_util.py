@@ -37,11 +37,12 @@ def sample_rows(L: int, topk: int, n: int, seed: int = 0):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def check_structure_all(idx_t, topk: int):
-    """Invariants on every row of a device index tensor: count, causality, order."""
+def check_structure_all(idx_t, topk: int, row0: int = 0):
+    """Invariants on every row of a device index tensor: count, causality,
+    order.  Row r holds query position row0 + r."""
     import torch
     L = idx_t.shape[0]
-    t = torch.arange(L, device=idx_t.device).unsqueeze(1)
+    t = torch.arange(row0, row0 + L, device=idx_t.device).unsqueeze(1)
     n = torch.clamp(t + 1, max=topk)
     pos = torch.arange(topk, device=idx_t.device).unsqueeze(0)
     valid = pos < n

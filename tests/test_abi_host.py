@@ -112,6 +112,20 @@ def test_prefill_rejects_before_any_device_call():
     assert _prefill(lib, L=20000, od=FAKE) == dsa.DSA_ERR_INVALID_ARG    # dense output limited
 
 
+def test_prefill_chunk_rejects_before_any_device_call():
+    lib = dsa.lib()
+
+    def call(q0=100, lq=50, H=64, D=128, topk=16, ws=FAKE, wsb=1 << 30, oi=FAKE):
+        return lib.dsa_indexer_topk_prefill_chunk(FAKE, None, 0, FAKE, None, FAKE, q0, lq, H, D, topk,
+                                                  dsa.DSA_FP8_E4M3, oi, None, ws, wsb, None)
+    assert call(q0=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert call(lq=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(q0=2**31 - 10, lq=20) == dsa.DSA_ERR_INVALID_ARG
+    assert call(oi=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
+    assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
+
+
 def test_decode_rejects_before_any_device_call():
     lib = dsa.lib()
     n = dsa.dsa_indexer_topk_decode_workspace(32, 131072, 64, 128, 2048)
