@@ -11,7 +11,8 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|prefill_32k_chunked|fs_47|fs_decode_47|mli_decode_47``)
+(``--workload tiny|prefill_196k|prefill_32k_chunked|decode_128k_paged|fs_47|fs_decode_47|
+mli_decode_47``)
 print their own line.
 """
 from __future__ import annotations
@@ -248,6 +249,8 @@ def run_workload(args):
                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                              "frac": round(tf / peak, 4), "traffic": None},
                 "config": {"workload": name, **{k: v for k, v in cfg.items() if k != "kind"}}}
+    if name == "decode_128k_paged":
+        return run_decode_paged(args, g, dsa, gen, stream)
     if name == "prefill_32k_chunked":
         return run_prefill_chunked(args, g, dsa, gen, stream)
     if name == "fs_47":
@@ -257,6 +260,41 @@ def run_workload(args):
     if name == "mli_decode_47":
         return run_mli_decode(args, g, dsa, gen, stream)
     raise SystemExit(f"unknown workload {name}")
+
+
+def run_decode_paged(args, g, dsa, gen, stream):
+    """The B=32 x 131072 decode with the cache in 64-token pages in a seeded
+    shuffled order, against the same cache stored contiguously (both timed
+    back to back on one copy of the data)."""
+    import torch
+    cfg = gen.CONFIGS["decode_128k"]
+    B, Lmax, H, D, topk = cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"], cfg["topk"]
+    P = 64
+    dev = g.device
+    d = g.decode_inputs(cfg)
+    mb = Lmax // P
+    perm = torch.randperm(B * mb, generator=torch.Generator().manual_seed(1)).to(dev)
+    pages = torch.empty((B * mb, P, D), dtype=torch.uint8, device=dev)
+    spages = torch.empty((B * mb, P), dtype=torch.float32, device=dev)
+    pages.index_copy_(0, perm, d["cache"].reshape(B * mb, P, D))
+    spages.index_copy_(0, perm, d["k_scale"].reshape(B * mb, P))
+    table = perm.to(torch.int32).reshape(B, mb).contiguous()
+    out = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsa.dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dtype=torch.uint8, device=dev)
+    contiguous = lambda: dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk,
+                                                     out_idx=out, workspace=ws, stream=stream)
+    paged = lambda: dsa.dsa_indexer_topk_decode_paged(d["q"], d["w"], pages, spages, table, d["lens"], topk,
+                                                      out_idx=out, workspace=ws, stream=stream)
+    t_c = sum(time_calls(contiguous, args.steps, args.warmup, stream)) / args.steps
+    t_p = sum(time_calls(paged, args.steps, args.warmup, stream)) / args.steps
+    nbytes = decode_bytes(gen.decode_lens(cfg), H, D, topk, B)
+    gbps = nbytes / (t_p * 1e-3) / 1e9
+    return {"metric": METRIC, "workload": "decode_128k_paged", "value": round(gbps, 1), "unit": "GB/s",
+            "paged_us": round(t_p * 1e3, 2), "contiguous_us": round(t_c * 1e3, 2), "page_size": P,
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+            "config": {"workload": "decode_128k_paged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
+                       "page_size": P}}
 
 
 def run_prefill_chunked(args, g, dsa, gen, stream):

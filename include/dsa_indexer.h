@@ -153,6 +153,30 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
                                    int32_t* out_idx, float* out_topk_score,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode over a paged key cache, as serving engines keep it ([IS] 2: the
+ * decode indexer scores each sequence's whole cache every step): the same
+ * selection as dsa_indexer_topk_decode on the cache the pages describe.
+ * k_pages       [num_pages, page_size, D] e4m3
+ * k_scale_pages [num_pages, page_size] fp32
+ * block_table   [B, max_blocks] int32, device: token s of sequence b is row
+ *               s % page_size of page block_table[b, s / page_size]
+ * page_size     a power of two >= 32; 1 <= max_blocks; the largest sequence
+ *               is max_blocks * page_size <= 262144 tokens.
+ * Entries for the blocks below ceil(len_b / page_size) must be page ids in
+ * [0, num_pages); others are not read.  (An id outside the range is clamped
+ * into it, so no access leaves the page arrays; the selection of that
+ * sequence is then unspecified.)  q, w, seq_lens, outputs and limits as for
+ * dsa_indexer_topk_decode; the workspace is
+ * dsa_indexer_topk_decode_workspace(B, max_blocks * page_size, H, D, topk).
+ */
+dsa_status dsa_indexer_topk_decode_paged(const uint16_t* q, const uint16_t* w, const uint8_t* k_pages,
+                                         const float* k_scale_pages, int num_pages, int page_size,
+                                         const int32_t* block_table, int max_blocks,
+                                         const int32_t* seq_lens, int B, int H, int D, int topk,
+                                         int32_t* out_idx, float* out_topk_score,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * IndexCache Full/Shared schedule.  [IC] 2.1, [BA] inference-loop figure,
  * [IS] 4.2.

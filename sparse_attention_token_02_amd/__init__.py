@@ -28,7 +28,7 @@ DSA_BF16, DSA_FP8_E4M3 = 0, 1
 EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
     "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill", "dsa_indexer_topk_prefill_chunk",
-    "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode",
+    "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode", "dsa_indexer_topk_decode_paged",
     "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers",
     "indexcache_greedy_search", "indexcache_overlap_proxy_loss", "mli_resolve",
     "indexcache_run_decode_layers_mli", "standin_sparse_attention_workspace", "standin_sparse_attention",
@@ -61,6 +61,9 @@ _lib.dsa_indexer_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32,
 _lib.dsa_indexer_topk_decode.restype = _i32
 _lib.dsa_indexer_topk_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                          _vp, _vp, _vp, _sz, _vp]
+_lib.dsa_indexer_topk_decode_paged.restype = _i32
+_lib.dsa_indexer_topk_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                               _vp, _vp, _vp, _sz, _vp]
 _lib.indexcache_resolve.restype = _i32
 _lib.indexcache_resolve.argtypes = [ctypes.c_char_p, _i32, ctypes.POINTER(ctypes.c_int32)]
 _lib.indexcache_run_layers.restype = _i32
@@ -223,6 +226,27 @@ def dsa_indexer_topk_decode(q, w, k_cache, k_scale, seq_lens, topk: int, *, out_
     _check(_lib.dsa_indexer_topk_decode(
         _ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(seq_lens), B, Lmax, H, D, topk,
         _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_topk_score
+
+
+def dsa_indexer_topk_decode_paged(q, w, k_pages, k_scale_pages, block_table, seq_lens, topk: int, *, out_idx=None,
+                                  out_topk_score=None, want_scores: bool = False, workspace=None, stream=None):
+    """q [B,H,D] bf16, w [B,H] bf16, k_pages [P,page,D] e4m3 codes, k_scale_pages
+    [P,page] fp32, block_table [B,max_blocks] int32, seq_lens [B] int32 (device).
+    Returns (idx [B,topk] int32, scores or None)."""
+    import torch
+    B, H, D = q.shape
+    num_pages, page = k_pages.shape[0], k_pages.shape[1]
+    max_blocks = block_table.shape[1]
+    dev = q.device
+    if out_idx is None:
+        out_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    if out_topk_score is None and want_scores:
+        out_topk_score = torch.empty((B, topk), dtype=torch.float32, device=dev)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, max_blocks * page, H, D, topk), dev, workspace)
+    _check(_lib.dsa_indexer_topk_decode_paged(
+        _ptr(q), _ptr(w), _ptr(k_pages), _ptr(k_scale_pages), num_pages, page, _ptr(block_table), max_blocks,
+        _ptr(seq_lens), B, H, D, topk, _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
     return out_idx, out_topk_score
 
 

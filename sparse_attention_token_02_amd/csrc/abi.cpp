@@ -193,6 +193,9 @@ struct DecodeArgs {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  // paged cache: Lmax = max_blocks * page_size
+  const int32_t* block_table = nullptr;
+  int max_blocks = 0, page_size = 0, num_pages = 0;
 };
 
 dsa_status validate_decode(const DecodeArgs& a) {
@@ -233,6 +236,10 @@ dsa_status launch_decode(const DecodeArgs& a) {
   p.bitmap = reinterpret_cast<uint32_t*>(base + lay.bitmap);
   p.cand_cnt = reinterpret_cast<int*>(base + lay.ccnt);
   p.cut = reinterpret_cast<int2*>(base + lay.cut);
+  p.block_table = a.block_table;
+  p.max_blocks = a.max_blocks;
+  p.page_shift = a.page_size > 0 ? __builtin_ctz((unsigned)a.page_size) : 0;
+  p.num_pages = a.num_pages;
   hipError_t e = dsa::decode_launch(p, a.H, a.D, a.stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return DSA_OK;
@@ -322,6 +329,31 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
                                    size_t workspace_bytes, void* stream) {
   DecodeArgs a{q, w, k_cache, k_scale, seq_lens, B, Lmax, H, D, topk, out_idx, out_topk_score, workspace,
                workspace_bytes, static_cast<hipStream_t>(stream)};
+  dsa_status st = validate_decode(a);
+  if (st != DSA_OK) return st;
+  st = launch_decode(a);
+  if (st != DSA_OK) return st;
+  return ok();
+}
+
+dsa_status dsa_indexer_topk_decode_paged(const uint16_t* q, const uint16_t* w, const uint8_t* k_pages,
+                                         const float* k_scale_pages, int num_pages, int page_size,
+                                         const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int B,
+                                         int H, int D, int topk, int32_t* out_idx, float* out_topk_score,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (page_size < 32 || (page_size & (page_size - 1)) != 0)
+    return fail(DSA_ERR_INVALID_ARG, "page_size must be a power of two >= 32 (got %d)", page_size);
+  if (num_pages < 1 || max_blocks < 1)
+    return fail(DSA_ERR_INVALID_ARG, "num_pages and max_blocks must be >= 1");
+  if ((int64_t)max_blocks * page_size > kMaxDecodeLmax)
+    return fail(DSA_ERR_UNSUPPORTED, "max_blocks * page_size must be <= %d", kMaxDecodeLmax);
+  if (!block_table) return fail(DSA_ERR_INVALID_ARG, "block_table must not be NULL");
+  DecodeArgs a{q, w, k_pages, k_scale_pages, seq_lens, B, max_blocks * page_size, H, D, topk, out_idx,
+               out_topk_score, workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  a.page_size = page_size;
+  a.num_pages = num_pages;
   dsa_status st = validate_decode(a);
   if (st != DSA_OK) return st;
   st = launch_decode(a);

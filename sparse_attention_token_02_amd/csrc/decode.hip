@@ -33,6 +33,7 @@ namespace {
 
 constexpr int DS_NT = 256;          // score kernel threads
 constexpr int DS_NSUB = 64;         // 32-key steps per wave
+static_assert(DS_NSUB <= 64, "paged lookup: one lane per step");
 #ifndef DS_PF_STEPS
 #define DS_PF_STEPS 4
 #endif
@@ -63,7 +64,7 @@ __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
 
 }  // namespace
 
-template <int H, int D>
+template <int H, int D, bool PAGED>
 __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) {
   constexpr int MB = (H + 31) / 32;
   constexpr int KS = D / 16;              // bf16 MFMA steps along D
@@ -100,8 +101,8 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   const int kh = lane >> 5;
   const int col = lane & 31;
 
-  const uint8_t* cache_b = p.cache + (size_t)b * p.Lmax * D;
-  const float* ks_b = p.k_scale + (size_t)b * p.Lmax;
+  const uint8_t* cache_b = PAGED ? p.cache : p.cache + (size_t)b * p.Lmax * D;
+  const float* ks_b = PAGED ? p.k_scale : p.k_scale + (size_t)b * p.Lmax;
   float* sc_b = p.scores + (size_t)b * p.ld;
   auto chunk_key = [&](int sub) { return 32 * ((sub * nwg + x) * WAVES + wave); };
 
@@ -138,20 +139,48 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // a load still in flight.
   v4i raw[DS_PF][NLD];
   float kss[DS_PF];
-  auto fetch = [&](int slot, int s0) {
+  // Paged cache: the 32 keys of a step (s0 a multiple of 32, pages of at
+  // least 32 keys), clamped to the sequence, all lie in the page of
+  // min(s0, len - 1).  Lane u of each wave looks up the page of its step u
+  // once (nstep <= 64), so a fetch reads it from a register instead of
+  // waiting for a table load.  Page ids outside [0, num_pages) are clamped
+  // into it (no access leaves the page array).
+  int step_page = 0;
+  if constexpr (PAGED) {
+    if (lane < nstep) {
+      const int sb = min(chunk_key(lane), len - 1);
+      step_page = p.block_table[(size_t)b * p.max_blocks + (sb >> p.page_shift)];
+      step_page = min(max(step_page, 0), p.num_pages - 1);
+    }
+  }
+  auto fetch = [&](int slot, int sub) {
+    const int s0 = chunk_key(sub);
+    const uint8_t* rows = cache_b;
+    const float* kss_p = ks_b;
+    int smask = 0;
+    if constexpr (PAGED) {
+      const int pg = __builtin_amdgcn_readlane(step_page, sub);
+      rows = p.cache + ((size_t)pg << p.page_shift) * D;
+      kss_p = p.k_scale + ((size_t)pg << p.page_shift);
+      smask = (1 << p.page_shift) - 1;
+    }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int byte = 1024 * i + 16 * lane;
       const int r = byte / D;
-      raw[slot][i] = *reinterpret_cast<const v4i*>(cache_b + (size_t)min(s0 + r, len - 1) * D + byte % D);
+      int s = min(s0 + r, len - 1);
+      if constexpr (PAGED) s &= smask;
+      raw[slot][i] = *reinterpret_cast<const v4i*>(rows + (size_t)s * D + byte % D);
     }
-    kss[slot] = ks_b[min(s0 + col, len - 1)];
+    int sk = min(s0 + col, len - 1);
+    if constexpr (PAGED) sk &= smask;
+    kss[slot] = kss_p[sk];
   };
   uint8_t* tr = ktr[wave];
   // this lane's operand chunks: key `col`, chunks kh*NLD + i of its row
   const int rswz = (col / RPB) % CPR;
 #pragma unroll
-  for (int u = 0; u < DS_PF; ++u) fetch(u, chunk_key(u));
+  for (int u = 0; u < DS_PF; ++u) fetch(u, u);
 
   for (int i = tid; i < HBINS; i += DS_NT) hist[i] = 0u;
   __syncthreads();
@@ -173,7 +202,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
           *reinterpret_cast<v4i*>(tr + r * D + 16 * (c ^ ((r / RPB) % CPR))) = raw[u][i];
         }
         const float cks = kss[u];
-        fetch(u, chunk_key(min(sub + DS_PF, nstep - 1)));   // past the end: harmless reload
+        fetch(u, min(sub + DS_PF, nstep - 1));   // past the end: harmless reload
         wave_lds_sync();
         v4i cur[NLD];
 #pragma unroll
@@ -648,7 +677,8 @@ DecodeWsSizes decode_ws_sizes(int Lmax) {
 template <int H, int D>
 static void launch_score(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(score_workgroups(p.Lmax), p.B);
-  hipLaunchKernelGGL((decode_score_kernel<H, D>), grid, dim3(DS_NT), 0, stream, p);
+  if (p.block_table) hipLaunchKernelGGL((decode_score_kernel<H, D, true>), grid, dim3(DS_NT), 0, stream, p);
+  else hipLaunchKernelGGL((decode_score_kernel<H, D, false>), grid, dim3(DS_NT), 0, stream, p);
 }
 
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream) {

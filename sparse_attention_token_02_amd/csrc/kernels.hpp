@@ -51,6 +51,13 @@ struct DecodeParams {
   int* cand_idx;             // workspace [B, Lmax]
   int* cand_cnt;             // workspace [B, cand_cnt]: candidates per select workgroup
   int2* cut;                 // workspace [B]: bin of the k-th score, keys in higher bins
+  // paged cache (block_table != null): cache = pages [num_pages, 2^page_shift, D],
+  // k_scale = [num_pages, 2^page_shift]; token s of sequence b lives in page
+  // block_table[b * max_blocks + (s >> page_shift)]; Lmax = max_blocks << page_shift
+  const int32_t* block_table;
+  int max_blocks;
+  int page_shift;
+  int num_pages;
 };
 
 struct DecodeWsSizes {

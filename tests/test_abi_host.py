@@ -145,6 +145,22 @@ def test_decode_rejects_before_any_device_call():
     assert call(c=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG
 
 
+def test_decode_paged_rejects_before_any_device_call():
+    lib = dsa.lib()
+
+    def call(page=64, npages=10, table=FAKE, mb=16, H=64, wsb=1 << 30, c=FAKE):
+        return lib.dsa_indexer_topk_decode_paged(FAKE, FAKE, c, FAKE, npages, page, table, mb, FAKE, 2, H, 128, 16,
+                                                 FAKE, None, FAKE, wsb, None)
+    assert call(page=48) == dsa.DSA_ERR_INVALID_ARG
+    assert call(page=16) == dsa.DSA_ERR_INVALID_ARG
+    assert call(npages=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(table=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(mb=8193) == dsa.DSA_ERR_UNSUPPORTED          # more than 262144 tokens
+    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(wsb=64) == dsa.DSA_ERR_WORKSPACE
+    assert call(c=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG
+
+
 def test_overlap_rejects_before_any_device_call():
     lib = dsa.lib()
     arr = (ctypes.c_void_p * 2)(FAKE, FAKE)
