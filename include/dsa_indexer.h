@@ -128,6 +128,30 @@ dsa_status dsa_indexer_topk_prefill_chunk(const void* q, const float* q_scale, i
                                           int32_t* out_idx, float* out_topk_score,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Ragged batch of sequences, packed: sequence i has the query rows
+ * cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 and the keys
+ * cu_seqlens_k[i] .. cu_seqlens_k[i+1]-1, its queries being the last
+ * Lq_i = cu_seqlens_q[i+1] - cu_seqlens_q[i] of its Lk_i keys (a chunk as in
+ * dsa_indexer_topk_prefill_chunk, q_offset = Lk_i - Lq_i; Lq_i = Lk_i is a
+ * whole sequence, Lq_i = 0 is skipped).  cu_seqlens_* are HOST int32 arrays
+ * of nseq + 1 entries starting at 0 and non-decreasing, with Lq_i <= Lk_i.
+ * q [total_q, H, D], q_scale ([total_q] or [total_q, H]), w [total_q, H],
+ * out_idx / out_topk_score [total_q, topk]; k [total_k, D], k_scale [total_k].
+ * Each row gets the selection of its own sequence, exactly as a call per
+ * sequence would.  One launch per non-empty sequence, longest key range
+ * first, on `stream`; the workspace (from the query below) is shared.
+ */
+dsa_status dsa_indexer_topk_prefill_varlen_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                                     int nseq, int H, int D, int topk, dsa_dtype dt,
+                                                     size_t* bytes);
+dsa_status dsa_indexer_topk_prefill_varlen(const void* q, const float* q_scale, int64_t q_scale_head_stride,
+                                           const void* k, const float* k_scale, const uint16_t* w,
+                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                                           int H, int D, int topk, dsa_dtype dt,
+                                           int32_t* out_idx, float* out_topk_score,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Decode: B sequences with one new query each, at position len_b - 1, whose
  * own key is already in the cache; the query scores the whole cache

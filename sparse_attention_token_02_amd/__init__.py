@@ -28,6 +28,7 @@ DSA_BF16, DSA_FP8_E4M3 = 0, 1
 EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
     "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill", "dsa_indexer_topk_prefill_chunk",
+    "dsa_indexer_topk_prefill_varlen_workspace", "dsa_indexer_topk_prefill_varlen",
     "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode", "dsa_indexer_topk_decode_paged",
     "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers",
     "indexcache_greedy_search", "indexcache_overlap_proxy_loss", "mli_resolve",
@@ -56,6 +57,13 @@ _lib.dsa_indexer_topk_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _
 _lib.dsa_indexer_topk_prefill_chunk.restype = _i32
 _lib.dsa_indexer_topk_prefill_chunk.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _vp, _vp, _vp, _sz, _vp]
+_lib.dsa_indexer_topk_prefill_varlen_workspace.restype = _i32
+_lib.dsa_indexer_topk_prefill_varlen_workspace.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                                           _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+_lib.dsa_indexer_topk_prefill_varlen.restype = _i32
+_lib.dsa_indexer_topk_prefill_varlen.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
+                                                 ctypes.POINTER(ctypes.c_int32), _i32, _i32, _i32, _i32, _i32, _vp,
+                                                 _vp, _vp, _sz, _vp]
 _lib.dsa_indexer_topk_decode_workspace.restype = _i32
 _lib.dsa_indexer_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 _lib.dsa_indexer_topk_decode.restype = _i32
@@ -200,6 +208,46 @@ def dsa_indexer_topk_prefill_chunk(q, q_scale, k, k_scale, w, q_offset: int, top
     ws = _workspace(dsa_indexer_topk_prefill_workspace(Lq, H, D, topk, dt), dev, workspace)
     _check(_lib.dsa_indexer_topk_prefill_chunk(
         _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), q_offset, Lq, H, D, topk,
+        _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_topk_score
+
+
+def _cu(xs):
+    xs = [int(v) for v in xs]
+    return (ctypes.c_int32 * len(xs))(*xs), len(xs) - 1
+
+
+def dsa_indexer_topk_prefill_varlen_workspace(cu_seqlens_q, cu_seqlens_k, H: int, D: int, topk: int, dt) -> int:
+    cq, n = _cu(cu_seqlens_q)
+    ck, nk = _cu(cu_seqlens_k)
+    if n != nk:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    v = _sz(0)
+    _check(_lib.dsa_indexer_topk_prefill_varlen_workspace(cq, ck, n, H, D, topk, _dt(dt), ctypes.byref(v)))
+    return v.value
+
+
+def dsa_indexer_topk_prefill_varlen(q, q_scale, k, k_scale, w, cu_seqlens_q, cu_seqlens_k, topk: int, dt, *,
+                                    q_scale_head_stride: int = 0, out_idx=None, out_topk_score=None,
+                                    want_scores: bool = False, workspace=None, stream=None):
+    """Packed ragged batch: q [total_q,H,D], w [total_q,H], k [total_k,D]; the
+    cu_seqlens are host sequences of nseq+1 ints.  Returns (idx [total_q,topk],
+    topk scores or None)."""
+    import torch
+    TQ, H, D = q.shape
+    dev = q.device
+    cq, n = _cu(cu_seqlens_q)
+    ck, nk = _cu(cu_seqlens_k)
+    if n != nk:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if out_idx is None:
+        out_idx = torch.empty((TQ, topk), dtype=torch.int32, device=dev)
+    if out_topk_score is None and want_scores:
+        out_topk_score = torch.empty((TQ, topk), dtype=torch.float32, device=dev)
+    ws = _workspace(dsa_indexer_topk_prefill_varlen_workspace(cu_seqlens_q, cu_seqlens_k, H, D, topk, dt), dev,
+                    workspace)
+    _check(_lib.dsa_indexer_topk_prefill_varlen(
+        _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), cq, ck, n, H, D, topk,
         _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
     return out_idx, out_topk_score
 

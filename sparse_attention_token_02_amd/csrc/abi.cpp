@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -308,6 +309,85 @@ dsa_status dsa_indexer_topk_prefill_chunk(const void* q, const float* q_scale, i
   if (st != DSA_OK) return st;
   st = launch_prefill(a);
   if (st != DSA_OK) return st;
+  return ok();
+}
+
+// Ragged batch: sequence i has query rows cu_q[i] .. cu_q[i+1]-1 (packed) at
+// the end of its keys cu_k[i] .. cu_k[i+1]-1.
+static dsa_status check_varlen(const int32_t* cu_q, const int32_t* cu_k, int nseq, int* max_lq) {
+  if (!cu_q || !cu_k) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must not be NULL");
+  if (nseq < 1) return fail(DSA_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
+  if (cu_q[0] != 0 || cu_k[0] != 0) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens must start at 0");
+  int m = 0;
+  for (int i = 0; i < nseq; ++i) {
+    const int lq = cu_q[i + 1] - cu_q[i], lk = cu_k[i + 1] - cu_k[i];
+    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i])
+      return fail(DSA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (sequence %d)", i);
+    if (lq > lk) return fail(DSA_ERR_INVALID_ARG, "sequence %d has more queries (%d) than keys (%d)", i, lq, lk);
+    m = lq > m ? lq : m;
+  }
+  *max_lq = m;
+  return DSA_OK;
+}
+
+dsa_status dsa_indexer_topk_prefill_varlen_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                                     int nseq, int H, int D, int topk, dsa_dtype dt,
+                                                     size_t* bytes) {
+  if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
+  int max_lq = 0;
+  dsa_status st = check_varlen(cu_seqlens_q, cu_seqlens_k, nseq, &max_lq);
+  if (st != DSA_OK) return st;
+  st = check_prefill_shape(max_lq > 0 ? max_lq : 1, H, D, topk, dt);
+  if (st != DSA_OK) return st;
+  *bytes = prefill_ws_bytes(max_lq > 0 ? max_lq : 1, H, D, topk, dt);
+  return ok();
+}
+
+dsa_status dsa_indexer_topk_prefill_varlen(const void* q, const float* q_scale, int64_t q_scale_head_stride,
+                                           const void* k, const float* k_scale, const uint16_t* w,
+                                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
+                                           int H, int D, int topk, dsa_dtype dt, int32_t* out_idx,
+                                           float* out_topk_score, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  size_t need = 0;
+  dsa_status st = dsa_indexer_topk_prefill_varlen_workspace(cu_seqlens_q, cu_seqlens_k, nseq, H, D, topk, dt, &need);
+  if (st != DSA_OK) return st;
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  const size_t qbytes = dt == DSA_FP8_E4M3 ? 1 : 2;
+  auto args = [&](int i) {
+    const int q0row = cu_seqlens_q[i], k0 = cu_seqlens_k[i];
+    const int lq = cu_seqlens_q[i + 1] - q0row, lk = cu_seqlens_k[i + 1] - k0;
+    PrefillArgs a{static_cast<const uint8_t*>(q) + (size_t)q0row * H * D * qbytes,
+                  q_scale ? q_scale + (size_t)q0row * (q_scale_head_stride ? H : 1) : nullptr, q_scale_head_stride,
+                  static_cast<const uint8_t*>(k) + (size_t)k0 * D * qbytes, k_scale ? k_scale + k0 : nullptr,
+                  w + (size_t)q0row * H, lq, H, D, topk, dt, out_idx + (size_t)q0row * topk,
+                  out_topk_score ? out_topk_score + (size_t)q0row * topk : nullptr, nullptr, workspace,
+                  workspace_bytes, static_cast<hipStream_t>(stream)};
+    a.q0 = lk - lq;
+    return a;
+  };
+  std::vector<int> order;
+  for (int i = 0; i < nseq; ++i) {
+    if (cu_seqlens_q[i + 1] == cu_seqlens_q[i]) continue;
+    st = validate_prefill(args(i));
+    if (st != DSA_OK) {
+      std::string m = g_err;
+      return fail(st, "sequence %d: %s", i, m.c_str());
+    }
+    order.push_back(i);
+  }
+  // the longest key range first
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return cu_seqlens_k[a + 1] - cu_seqlens_k[a] > cu_seqlens_k[b + 1] - cu_seqlens_k[b];
+  });
+  for (int i : order) {
+    st = launch_prefill(args(i));
+    if (st != DSA_OK) {
+      std::string m = g_err;
+      return fail(st, "sequence %d: %s", i, m.c_str());
+    }
+  }
   return ok();
 }
 

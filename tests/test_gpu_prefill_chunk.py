@@ -87,3 +87,47 @@ def test_chunk_32k_tail_equals_whole_run(dsa):
         q0 = L - 8192 + 2048 * j
         idx_j, _ = _chunk(dsa, d, q0, 2048, topk, "fp8")
         assert torch.equal(idx_j, idx_w[q0:q0 + 2048]), j
+
+
+def test_varlen_batch_equals_per_sequence_calls(dsa):
+    """A packed ragged batch: whole sequences, chunks at the end of longer key
+    ranges, a one-token sequence and an empty query range; each sequence's
+    rows equal its own call byte for byte, and the oracle on sampled rows."""
+    import torch
+    base = gen.CONFIGS["prefill_32k"]
+    topk = 128
+    seqs = [(3000, 3000), (1200, 5003), (1, 1), (0, 700), (257, 257), (64, 2500)]   # (Lq, Lk)
+    parts = []
+    for i, (lq, lk) in enumerate(seqs):
+        cfg = dict(base, L=lk, topk=topk, heavy_count=max(1, lk // 100), seed=10 + i)
+        parts.append(gen.prefill_inputs(cfg))
+    rows_of = [np.arange(lk - lq, lk) for lq, lk in seqs]
+    cat = lambda key, sl: np.concatenate([p[key][sl(i)] for i, p in enumerate(parts)])
+    q = cat("q", lambda i: rows_of[i])
+    qs = cat("q_scale", lambda i: rows_of[i])
+    w = cat("w", lambda i: rows_of[i])
+    k = cat("k", lambda i: slice(None))
+    ks = cat("k_scale", lambda i: slice(None))
+    cu_q = np.concatenate([[0], np.cumsum([lq for lq, _ in seqs])]).tolist()
+    cu_k = np.concatenate([[0], np.cumsum([lk for _, lk in seqs])]).tolist()
+    note("prefill varlen 6 sequences")
+    idx, sc = dsa.dsa_indexer_topk_prefill_varlen(dev(q), dev(qs), dev(k), dev(ks), dev(w), cu_q, cu_k, topk, "fp8",
+                                                  want_scores=True)
+    torch.cuda.synchronize()
+    for i, (lq, lk) in enumerate(seqs):
+        if lq == 0:
+            continue
+        p = parts[i]
+        r = rows_of[i]
+        one, one_sc = dsa.dsa_indexer_topk_prefill_chunk(dev(p["q"][r]), dev(p["q_scale"][r]), dev(p["k"]),
+                                                         dev(p["k_scale"]), dev(p["w"][r]), lk - lq, topk, "fp8",
+                                                         want_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(idx[cu_q[i]:cu_q[i + 1]], one), i
+        assert torch.equal(sc[cu_q[i]:cu_q[i + 1]], one_sc), i
+        pick = np.unique(np.linspace(0, lq - 1, 6).astype(int))
+        res = oracle.prefill(p["q"][r][pick], p["q_scale"][r][pick], p["k"], p["k_scale"], p["w"][r][pick], "fp8",
+                             topk, rows=r[pick], return_scores=True)
+        ih = host(idx[cu_q[i]:cu_q[i + 1]])
+        for j, t in enumerate(pick):
+            assert parity.check_row(ih[t], res["o"][j], res["A"][j], topk) is None, (i, t)
