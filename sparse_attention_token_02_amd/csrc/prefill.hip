@@ -591,8 +591,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         if (t >= L) continue;
         int* dix = p.out_idx + (size_t)(t - p.q0) * p.topk;
         float* dsc = p.out_score ? p.out_score + (size_t)(t - p.q0) * p.topk : nullptr;
-        wave_select<true>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix,
-                          p.topk, sh.whist[wave], nullptr, lbuf, lcap);
+        wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix, p.topk,
+                    sh.whist[wave], nullptr, lbuf, lcap);
       }
       break;
     }

@@ -181,20 +181,8 @@ __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int k
 // lbuf (16-byte aligned wave-private LDS of lcap floats, lcap a multiple of
 // 4, or null): when the list fits, its scores are copied there once and every
 // later pass reads them from LDS (then dsc must not alias sc).
-// STREAM_OUT: the destination is written once and not read again by the
-// kernel, so it is stored with the non-temporal hint and does not linger as
-// dirty cache lines that the next kernel would have to write back.
-template <bool STREAM_OUT = false>
 __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
                            uint32_t* hist, float* tau, float* lbuf = nullptr, int lcap = 0) {
-  auto put_i = [](int* d, int v) {
-    if constexpr (STREAM_OUT) __builtin_nontemporal_store(v, d);
-    else *d = v;
-  };
-  auto put_f = [](float* d, float v) {
-    if constexpr (STREAM_OUT) __builtin_nontemporal_store(v, d);
-    else *d = v;
-  };
   const int lane = __lane_id();
   WaveCut cut{0u, 0u, 0xFFFFFFFFu, 0u};   // keeps everything
   const float* ksc = sc;                  // where the scores are read from
@@ -284,8 +272,8 @@ __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* 
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((take >> e) & 1u) {
-          put_i(dix + pos, iv[u][e]);
-          if (dsc) put_f(dsc + pos, sv[u][e]);
+          dix[pos] = iv[u][e];
+          if (dsc) dsc[pos] = sv[u][e];
           ++pos;
         }
       out += __builtin_amdgcn_readlane(nt_incl, 63);
@@ -293,8 +281,8 @@ __device__ int wave_select(const float* sc, const int* ix, int n, int k, float* 
     }
   }
   for (int e = out + lane; e < pad_to; e += 64) {
-    put_i(dix + e, -1);
-    if (dsc) put_f(dsc + e, -__builtin_inff());
+    dix[e] = -1;
+    if (dsc) dsc[e] = -__builtin_inff();
   }
   return out;
 }
