@@ -11,8 +11,8 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|prefill_32k_chunked|decode_128k_paged|fs_47|fs_decode_47|
-mli_decode_47``)
+(``--workload tiny|prefill_196k|prefill_32k_chunked|prefill_ragged|decode_128k_paged|fs_47|
+fs_decode_47|mli_decode_47``)
 print their own line.
 """
 from __future__ import annotations
@@ -249,6 +249,8 @@ def run_workload(args):
                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                              "frac": round(tf / peak, 4), "traffic": None},
                 "config": {"workload": name, **{k: v for k, v in cfg.items() if k != "kind"}}}
+    if name == "prefill_ragged":
+        return run_prefill_ragged(args, g, dsa, gen, stream)
     if name == "decode_128k_paged":
         return run_decode_paged(args, g, dsa, gen, stream)
     if name == "prefill_32k_chunked":
@@ -295,6 +297,44 @@ def run_decode_paged(args, g, dsa, gen, stream):
                          "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
             "config": {"workload": "decode_128k_paged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
                        "page_size": P}}
+
+
+def run_prefill_ragged(args, g, dsa, gen, stream):
+    """A packed batch of 24 whole sequences of seeded lengths in [512, 16384]
+    (fp8, H=64, D=128, k=2048): one ragged launch, against one call per
+    sequence on the same data."""
+    import numpy as np
+    import torch
+    base = gen.CONFIGS["prefill_32k"]
+    H, D, topk = base["H"], base["D"], base["topk"]
+    lens = gen.uniform_int(7, gen.STREAM["lens"] * 1024 + 7, np.arange(24, dtype=np.uint64), 512, 16384)
+    lens = [int(x) for x in lens]
+    parts = [g.prefill_inputs(dict(base, L=n, heavy_count=max(1, n // 100), seed=100 + i)) for i, n in enumerate(lens)]
+    cat = lambda key: torch.cat([p[key] for p in parts])
+    q, qs, k, ks, w = cat("q"), cat("q_scale"), cat("k"), cat("k_scale"), cat("w")
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32, device=g.device)
+    out = torch.empty((q.shape[0], topk), dtype=torch.int32, device=g.device)
+    ws = torch.empty(dsa.dsa_indexer_topk_prefill_varlen_workspace(len(lens), q.shape[0], H, D, topk, "fp8"),
+                     dtype=torch.uint8, device=g.device)
+    wss = torch.empty(dsa.dsa_indexer_topk_prefill_workspace(max(lens), H, D, topk, "fp8"), dtype=torch.uint8,
+                      device=g.device)
+    ragged = lambda: dsa.dsa_indexer_topk_prefill_varlen(q, qs, k, ks, w, cu, cu, topk, "fp8", out_idx=out,
+                                                         workspace=ws, stream=stream)
+
+    def per_sequence():
+        for i, p in enumerate(parts):
+            dsa.dsa_indexer_topk_prefill(p["q"], p["q_scale"], p["k"], p["k_scale"], p["w"], topk, "fp8",
+                                         out_idx=out[int(cu[i]):int(cu[i]) + lens[i]], workspace=wss, stream=stream)
+    t_r = sum(time_calls(ragged, args.steps, args.warmup, stream)) / args.steps
+    t_s = sum(time_calls(per_sequence, args.steps, args.warmup, stream)) / args.steps
+    flops = sum(prefill_flops(n, H, D) for n in lens)
+    tf = flops / (t_r * 1e-3) / 1e12
+    return {"metric": METRIC, "workload": "prefill_ragged", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ragged_ms": round(t_r, 4), "per_sequence_calls_ms": round(t_s, 4), "lengths": lens,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+            "config": {"workload": "prefill_ragged", "sequences": len(lens), "total_rows": int(sum(lens)), "H": H,
+                       "D": D, "topk": topk}}
 
 
 def run_prefill_chunked(args, g, dsa, gen, stream):

@@ -129,26 +129,31 @@ dsa_status dsa_indexer_topk_prefill_chunk(const void* q, const float* q_scale, i
                                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Ragged batch of sequences, packed: sequence i has the query rows
- * cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 and the keys
+ * Ragged batch of sequences, packed, in one launch: sequence i has the query
+ * rows cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 and the keys
  * cu_seqlens_k[i] .. cu_seqlens_k[i+1]-1, its queries being the last
  * Lq_i = cu_seqlens_q[i+1] - cu_seqlens_q[i] of its Lk_i keys (a chunk as in
  * dsa_indexer_topk_prefill_chunk, q_offset = Lk_i - Lq_i; Lq_i = Lk_i is a
- * whole sequence, Lq_i = 0 is skipped).  cu_seqlens_* are HOST int32 arrays
- * of nseq + 1 entries starting at 0 and non-decreasing, with Lq_i <= Lk_i.
+ * whole sequence, Lq_i = 0 contributes nothing).
+ * cu_seqlens_q, cu_seqlens_k  DEVICE int32 [nseq + 1], read on the device:
+ *            a sequence whose bounds are not 0 <= cu_q[i] <= cu_q[i+1] <=
+ *            total_q, 0 <= cu_k[i] <= cu_k[i+1] <= total_k, Lq_i <= Lk_i is
+ *            skipped (its rows are not written); nothing is read or written
+ *            outside the arrays below whatever they hold.
  * q [total_q, H, D], q_scale ([total_q] or [total_q, H]), w [total_q, H],
  * out_idx / out_topk_score [total_q, topk]; k [total_k, D], k_scale [total_k].
  * Each row gets the selection of its own sequence, exactly as a call per
- * sequence would.  One launch per non-empty sequence, longest key range
- * first, on `stream`; the workspace (from the query below) is shared.
+ * sequence would.  A one-workgroup kernel builds the work-item table on the
+ * device (sequences longest first when nseq <= 1024, each sequence's
+ * longest items first); one persistent launch then takes items from it.
+ * Other arguments and limits as for dsa_indexer_topk_prefill.
  */
-dsa_status dsa_indexer_topk_prefill_varlen_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                                     int nseq, int H, int D, int topk, dsa_dtype dt,
+dsa_status dsa_indexer_topk_prefill_varlen_workspace(int nseq, int total_q, int H, int D, int topk, dsa_dtype dt,
                                                      size_t* bytes);
 dsa_status dsa_indexer_topk_prefill_varlen(const void* q, const float* q_scale, int64_t q_scale_head_stride,
                                            const void* k, const float* k_scale, const uint16_t* w,
                                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
-                                           int H, int D, int topk, dsa_dtype dt,
+                                           int total_q, int total_k, int H, int D, int topk, dsa_dtype dt,
                                            int32_t* out_idx, float* out_topk_score,
                                            void* workspace, size_t workspace_bytes, void* stream);
 

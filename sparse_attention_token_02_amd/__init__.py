@@ -58,12 +58,10 @@ _lib.dsa_indexer_topk_prefill_chunk.restype = _i32
 _lib.dsa_indexer_topk_prefill_chunk.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_indexer_topk_prefill_varlen_workspace.restype = _i32
-_lib.dsa_indexer_topk_prefill_varlen_workspace.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
-                                                           _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+_lib.dsa_indexer_topk_prefill_varlen_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 _lib.dsa_indexer_topk_prefill_varlen.restype = _i32
-_lib.dsa_indexer_topk_prefill_varlen.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, ctypes.POINTER(ctypes.c_int32),
-                                                 ctypes.POINTER(ctypes.c_int32), _i32, _i32, _i32, _i32, _i32, _vp,
-                                                 _vp, _vp, _sz, _vp]
+_lib.dsa_indexer_topk_prefill_varlen.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _vp, _vp, _vp, _sz, _vp]
 _lib.dsa_indexer_topk_decode_workspace.restype = _i32
 _lib.dsa_indexer_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 _lib.dsa_indexer_topk_decode.restype = _i32
@@ -212,43 +210,34 @@ def dsa_indexer_topk_prefill_chunk(q, q_scale, k, k_scale, w, q_offset: int, top
     return out_idx, out_topk_score
 
 
-def _cu(xs):
-    xs = [int(v) for v in xs]
-    return (ctypes.c_int32 * len(xs))(*xs), len(xs) - 1
-
-
-def dsa_indexer_topk_prefill_varlen_workspace(cu_seqlens_q, cu_seqlens_k, H: int, D: int, topk: int, dt) -> int:
-    cq, n = _cu(cu_seqlens_q)
-    ck, nk = _cu(cu_seqlens_k)
-    if n != nk:
-        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+def dsa_indexer_topk_prefill_varlen_workspace(nseq: int, total_q: int, H: int, D: int, topk: int, dt) -> int:
     v = _sz(0)
-    _check(_lib.dsa_indexer_topk_prefill_varlen_workspace(cq, ck, n, H, D, topk, _dt(dt), ctypes.byref(v)))
+    _check(_lib.dsa_indexer_topk_prefill_varlen_workspace(nseq, total_q, H, D, topk, _dt(dt), ctypes.byref(v)))
     return v.value
 
 
 def dsa_indexer_topk_prefill_varlen(q, q_scale, k, k_scale, w, cu_seqlens_q, cu_seqlens_k, topk: int, dt, *,
                                     q_scale_head_stride: int = 0, out_idx=None, out_topk_score=None,
                                     want_scores: bool = False, workspace=None, stream=None):
-    """Packed ragged batch: q [total_q,H,D], w [total_q,H], k [total_k,D]; the
-    cu_seqlens are host sequences of nseq+1 ints.  Returns (idx [total_q,topk],
-    topk scores or None)."""
+    """Packed ragged batch in one launch: q [total_q,H,D], w [total_q,H],
+    k [total_k,D]; cu_seqlens_* are device int32 tensors of nseq+1 entries.
+    Returns (idx [total_q,topk], topk scores or None)."""
     import torch
     TQ, H, D = q.shape
+    TK = k.shape[0]
     dev = q.device
-    cq, n = _cu(cu_seqlens_q)
-    ck, nk = _cu(cu_seqlens_k)
-    if n != nk:
+    nseq = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != nseq + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     if out_idx is None:
         out_idx = torch.empty((TQ, topk), dtype=torch.int32, device=dev)
     if out_topk_score is None and want_scores:
         out_topk_score = torch.empty((TQ, topk), dtype=torch.float32, device=dev)
-    ws = _workspace(dsa_indexer_topk_prefill_varlen_workspace(cu_seqlens_q, cu_seqlens_k, H, D, topk, dt), dev,
-                    workspace)
+    ws = _workspace(dsa_indexer_topk_prefill_varlen_workspace(nseq, TQ, H, D, topk, dt), dev, workspace)
     _check(_lib.dsa_indexer_topk_prefill_varlen(
-        _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), cq, ck, n, H, D, topk,
-        _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), nseq, TQ, TK, H, D, topk, _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws),
+        ws.numel(), _stream(stream)))
     return out_idx, out_topk_score
 
 

@@ -312,82 +312,90 @@ dsa_status dsa_indexer_topk_prefill_chunk(const void* q, const float* q_scale, i
   return ok();
 }
 
-// Ragged batch: sequence i has query rows cu_q[i] .. cu_q[i+1]-1 (packed) at
-// the end of its keys cu_k[i] .. cu_k[i+1]-1.
-static dsa_status check_varlen(const int32_t* cu_q, const int32_t* cu_k, int nseq, int* max_lq) {
-  if (!cu_q || !cu_k) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must not be NULL");
-  if (nseq < 1) return fail(DSA_ERR_INVALID_ARG, "nseq must be >= 1 (got %d)", nseq);
-  if (cu_q[0] != 0 || cu_k[0] != 0) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens must start at 0");
-  int m = 0;
-  for (int i = 0; i < nseq; ++i) {
-    const int lq = cu_q[i + 1] - cu_q[i], lk = cu_k[i + 1] - cu_k[i];
-    if (cu_q[i + 1] < cu_q[i] || cu_k[i + 1] < cu_k[i])
-      return fail(DSA_ERR_INVALID_ARG, "cu_seqlens must be non-decreasing (sequence %d)", i);
-    if (lq > lk) return fail(DSA_ERR_INVALID_ARG, "sequence %d has more queries (%d) than keys (%d)", i, lq, lk);
-    m = lq > m ? lq : m;
-  }
-  *max_lq = m;
-  return DSA_OK;
+// Ragged batch workspace: header (work counter at 0, item count at 128), the
+// item table (int4 per item), then the candidate lists of every slot.
+struct VarlenWs {
+  size_t items, lists, total;
+  int cap_items, slots;
+};
+
+static bool varlen_ws(int nseq, int total_q, int H, int D, int topk, dsa_dtype dt, VarlenWs* w) {
+  const int rw = dsa::prefill_rows_per_item(H);
+  const int64_t cap = ((int64_t)total_q + rw - 1) / rw + nseq;
+  if (cap > INT32_MAX / 2) return false;
+  w->cap_items = (int)cap;
+  w->slots = w->cap_items < kMaxSlots ? w->cap_items : kMaxSlots;
+  if (w->slots < 1) w->slots = 1;
+  w->items = kHeader;
+  w->lists = w->items + align_up((size_t)w->cap_items * 16, 256);
+  const size_t per = (size_t)rw * prefill_cap((int)dt, H, D, topk);
+  w->total = w->lists + 2 * align_up((size_t)w->slots * per * 4, 256);
+  return true;
 }
 
-dsa_status dsa_indexer_topk_prefill_varlen_workspace(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
-                                                     int nseq, int H, int D, int topk, dsa_dtype dt,
+dsa_status dsa_indexer_topk_prefill_varlen_workspace(int nseq, int total_q, int H, int D, int topk, dsa_dtype dt,
                                                      size_t* bytes) {
   if (!bytes) return fail(DSA_ERR_INVALID_ARG, "bytes must not be NULL");
-  int max_lq = 0;
-  dsa_status st = check_varlen(cu_seqlens_q, cu_seqlens_k, nseq, &max_lq);
+  if (nseq < 1 || total_q < 0) return fail(DSA_ERR_INVALID_ARG, "nseq must be >= 1 and total_q >= 0");
+  dsa_status st = check_prefill_shape(1, H, D, topk, dt);
   if (st != DSA_OK) return st;
-  st = check_prefill_shape(max_lq > 0 ? max_lq : 1, H, D, topk, dt);
-  if (st != DSA_OK) return st;
-  *bytes = prefill_ws_bytes(max_lq > 0 ? max_lq : 1, H, D, topk, dt);
+  VarlenWs w;
+  if (!varlen_ws(nseq, total_q, H, D, topk, dt, &w)) return fail(DSA_ERR_INVALID_ARG, "batch too large");
+  *bytes = w.total;
   return ok();
 }
 
 dsa_status dsa_indexer_topk_prefill_varlen(const void* q, const float* q_scale, int64_t q_scale_head_stride,
                                            const void* k, const float* k_scale, const uint16_t* w,
                                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int nseq,
-                                           int H, int D, int topk, dsa_dtype dt, int32_t* out_idx,
-                                           float* out_topk_score, void* workspace, size_t workspace_bytes,
-                                           void* stream) {
+                                           int total_q, int total_k, int H, int D, int topk, dsa_dtype dt,
+                                           int32_t* out_idx, float* out_topk_score, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
   size_t need = 0;
-  dsa_status st = dsa_indexer_topk_prefill_varlen_workspace(cu_seqlens_q, cu_seqlens_k, nseq, H, D, topk, dt, &need);
+  dsa_status st = dsa_indexer_topk_prefill_varlen_workspace(nseq, total_q, H, D, topk, dt, &need);
   if (st != DSA_OK) return st;
+  if (total_k < 0) return fail(DSA_ERR_INVALID_ARG, "total_k must be >= 0");
+  if (!cu_seqlens_q || !cu_seqlens_k) return fail(DSA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must not be NULL");
+  if (total_q == 0 || total_k == 0) return ok();   // nothing to select
+  if (!q || !k || !w || !out_idx) return fail(DSA_ERR_INVALID_ARG, "q, k, w and out_idx must not be NULL");
+  if (!aligned16(q) || !aligned16(k)) return fail(DSA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if (q_scale_head_stride != 0 && q_scale_head_stride != 1)
+    return fail(DSA_ERR_INVALID_ARG, "q_scale_head_stride must be 0 or 1");
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
-  const size_t qbytes = dt == DSA_FP8_E4M3 ? 1 : 2;
-  auto args = [&](int i) {
-    const int q0row = cu_seqlens_q[i], k0 = cu_seqlens_k[i];
-    const int lq = cu_seqlens_q[i + 1] - q0row, lk = cu_seqlens_k[i + 1] - k0;
-    PrefillArgs a{static_cast<const uint8_t*>(q) + (size_t)q0row * H * D * qbytes,
-                  q_scale ? q_scale + (size_t)q0row * (q_scale_head_stride ? H : 1) : nullptr, q_scale_head_stride,
-                  static_cast<const uint8_t*>(k) + (size_t)k0 * D * qbytes, k_scale ? k_scale + k0 : nullptr,
-                  w + (size_t)q0row * H, lq, H, D, topk, dt, out_idx + (size_t)q0row * topk,
-                  out_topk_score ? out_topk_score + (size_t)q0row * topk : nullptr, nullptr, workspace,
-                  workspace_bytes, static_cast<hipStream_t>(stream)};
-    a.q0 = lk - lq;
-    return a;
-  };
-  std::vector<int> order;
-  for (int i = 0; i < nseq; ++i) {
-    if (cu_seqlens_q[i + 1] == cu_seqlens_q[i]) continue;
-    st = validate_prefill(args(i));
-    if (st != DSA_OK) {
-      std::string m = g_err;
-      return fail(st, "sequence %d: %s", i, m.c_str());
-    }
-    order.push_back(i);
-  }
-  // the longest key range first
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-    return cu_seqlens_k[a + 1] - cu_seqlens_k[a] > cu_seqlens_k[b + 1] - cu_seqlens_k[b];
-  });
-  for (int i : order) {
-    st = launch_prefill(args(i));
-    if (st != DSA_OK) {
-      std::string m = g_err;
-      return fail(st, "sequence %d: %s", i, m.c_str());
-    }
-  }
+  if (!aligned16(workspace)) return fail(DSA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  int cus = 0;
+  if (device_cus(&cus) != 0) return fail(DSA_ERR_HIP, "no HIP device");
+  VarlenWs lay;
+  varlen_ws(nseq, total_q, H, D, topk, dt, &lay);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  const int rw = dsa::prefill_rows_per_item(H);
+  dsa::PrefillParams p{};
+  p.q = static_cast<const uint8_t*>(q);
+  p.q_scale = q_scale;
+  p.qs_row = q_scale_head_stride ? H : 1;
+  p.qs_head = q_scale_head_stride;
+  p.k = static_cast<const uint8_t*>(k);
+  p.k_scale = k_scale;
+  p.w = w;
+  p.topk = topk;
+  p.cap = prefill_cap((int)dt, H, D, topk);
+  p.sample_m = dsa::prefill_sample_keys((int)dt, H, D);
+  p.out_idx = out_idx;
+  p.out_score = out_topk_score;
+  p.counter = reinterpret_cast<int*>(base);
+  p.items = reinterpret_cast<const int4*>(base + lay.items);
+  p.n_items_dev = reinterpret_cast<const int*>(base + 128);
+  p.ws_sc = reinterpret_cast<float*>(base + lay.lists);
+  p.ws_ix = reinterpret_cast<int32_t*>(base + lay.lists + align_up((size_t)lay.slots * rw * p.cap * 4, 256));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dsa::prefill_varlen_prepare(cu_seqlens_q, cu_seqlens_k, nseq, total_q, total_k, rw,
+                                             reinterpret_cast<int4*>(base + lay.items), reinterpret_cast<int*>(base + 128),
+                                             p.counter, s);
+  if (e != hipSuccess) return hip_fail(e, "ragged batch prepare");
+  const int grid = lay.slots < cus ? lay.slots : cus;
+  e = dsa::prefill_launch(p, (int)dt, H, D, grid, s);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return ok();
 }
 

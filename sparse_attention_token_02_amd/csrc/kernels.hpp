@@ -30,7 +30,21 @@ struct PrefillParams {
   int32_t* ws_ix;            // [grid, rows_per_item, cap]
   int* counter;              // work counter
   int n_items;               // ceil((L - q0) / rows_per_item)
+  // Ragged batch (items != null): item i reads its sequence from items[i] =
+  // {q row of position 0 (q row of position t is t + x), first key row, key
+  // count, first query position of the item}, *n_items_dev items in all; L,
+  // q0 and n_items above are then unused.
+  const int4* items;
+  const int* n_items_dev;
 };
+
+// Builds the ragged-batch item table from device cu_seqlens (one workgroup):
+// sequences whose bounds are not 0 <= cu_q[i] <= cu_q[i+1] <= total_q,
+// 0 <= cu_k[i] <= cu_k[i+1] <= total_k, Lq <= Lk are skipped; the longest
+// key range goes first (by sequence, when nseq <= 1024), and within a
+// sequence its longest item first.  Also clears the work counter.
+hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int nseq, int total_q, int total_k,
+                                  int rows_per_item, int4* items, int* n_items, int* counter, hipStream_t stream);
 
 struct DecodeParams {
   const uint16_t* q;         // [B, H, D] bf16

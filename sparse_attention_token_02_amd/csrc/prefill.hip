@@ -158,7 +158,6 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
   const size_t slot_elems = (size_t)C::RW * p.cap;
   float* wsc = p.ws_sc + (size_t)blockIdx.x * slot_elems;
   int* wix = p.ws_ix + (size_t)blockIdx.x * slot_elems;
-  const int L = p.L;
 
   // A-operand row `col` of block mb holds the (query slot, head) of the result
   // row with the same index: result row m has lane half (m>>2)&1 and register
@@ -173,8 +172,27 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     if (tid == 0) sh.item = atomicAdd(p.counter, 1);
     __syncthreads();
     const int item = sh.item;
-    if (item >= p.n_items) break;
-    const int t0 = p.q0 + (p.n_items - 1 - item) * C::RW;
+    // the item's sequence: key count L, its keys, and the q/w/output row of
+    // query position t (t + qoff)
+    int L, t0, qoff;
+    const uint8_t* kp;
+    const float* ksp;
+    if (p.items) {
+      if (item >= *p.n_items_dev) break;
+      const int4 it = p.items[item];
+      qoff = it.x;
+      kp = p.k + (size_t)it.y * C::ROWB;
+      ksp = p.k_scale ? p.k_scale + it.y : nullptr;
+      L = it.z;
+      t0 = it.w;
+    } else {
+      if (item >= p.n_items) break;
+      qoff = -p.q0;
+      kp = p.k;
+      ksp = p.k_scale;
+      L = p.L;
+      t0 = p.q0 + (p.n_items - 1 - item) * C::RW;
+    }
     const int kend = min(t0 + C::RW, L);
     const int ntiles = (kend + C::TK - 1) / C::TK;
 
@@ -188,7 +206,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           if (t < L) {
-            const uint8_t* src = p.q + ((size_t)(t - p.q0) * H + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
+            const uint8_t* src = p.q + ((size_t)(t + qoff) * H + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
             qa[mb][ks] = load_opnd<C::FP8>(src);
           } else {
             qa[mb][ks] = zero_opnd<C::FP8>();
@@ -202,8 +220,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       const int t = t0 + i / H, head = i % H;
       float v = 0.f;
       if (t < L) {
-        v = bf16_to_f32(p.w[(size_t)(t - p.q0) * H + head]);
-        if (p.q_scale) v *= p.q_scale[(size_t)(t - p.q0) * p.qs_row + (size_t)head * p.qs_head];
+        v = bf16_to_f32(p.w[(size_t)(t + qoff) * H + head]);
+        if (p.q_scale) v *= p.q_scale[(size_t)(t + qoff) * p.qs_row + (size_t)head * p.qs_head];
       }
       sh.weff[i] = v;
     }
@@ -235,7 +253,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int pos = 64 * g + lane;
         const int r = pos / C::CPR;
         const int c = (pos % C::CPR) ^ ((r / C::RPB) & (C::CPR - 1));
-        const uint8_t* src = p.k + (size_t)min(kt + r, L - 1) * C::ROWB + c * 16;
+        const uint8_t* src = kp + (size_t)min(kt + r, L - 1) * C::ROWB + c * 16;
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                          (__attribute__((address_space(3))) void*)(tdst + 1024 * g), 16, 0, 0);
       }
@@ -243,8 +261,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         // H >= 32 reads k_scale lane-major: key 64*pair + lane at lane*(TK/64) + pair
         const int pos = 64 * wave + lane;
         const int kk = C::SPLIT ? 64 * (pos % (C::TK / 64)) + pos / (C::TK / 64) : pos;
-        if (p.k_scale) {
-          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(p.k_scale + min(kt + kk, L - 1)),
+        if (ksp) {
+          __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(ksp + min(kt + kk, L - 1)),
                                            (__attribute__((address_space(3))) void*)(kdst + 64 * wave), 4, 0, 0);
         } else {
           kdst[pos] = 1.f;
@@ -463,7 +481,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
             tile_scores(tile, ksc_t, [&](int pair, float score) {
               const int s = kt + 64 * pair + lane;
               if constexpr (DENSE) {
-                if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)(tr - p.q0) * L + s] = s <= tr ? score : -__builtin_inff();
+                if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)(tr + qoff) * L + s] = s <= tr ? score : -__builtin_inff();
               }
               const bool pass = (s <= tr) && (score > thr[0]);
               const uint64_t m = ballot64(pass);
@@ -483,7 +501,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
                 const float score = sc[r];
                 const int tr = t0 + row_base + r;
                 if constexpr (DENSE) {
-                  if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)(tr - p.q0) * L + s] = s <= tr ? score : -__builtin_inff();
+                  if (attempt == 0 && tr < L && s < L) p.out_dense[(size_t)(tr + qoff) * L + s] = s <= tr ? score : -__builtin_inff();
                 }
                 const bool pass = (s <= tr) && (score > thr[r]);
                 const uint64_t m = ballot64(pass);
@@ -589,8 +607,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int row = wave * C::QPW + rr;
         const int t = t0 + row;
         if (t >= L) continue;
-        int* dix = p.out_idx + (size_t)(t - p.q0) * p.topk;
-        float* dsc = p.out_score ? p.out_score + (size_t)(t - p.q0) * p.topk : nullptr;
+        int* dix = p.out_idx + (size_t)(t + qoff) * p.topk;
+        float* dsc = p.out_score ? p.out_score + (size_t)(t + qoff) * p.topk : nullptr;
         wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix, p.topk,
                     sh.whist[wave], nullptr, lbuf, lcap);
       }
@@ -605,6 +623,94 @@ __global__ void prefill_prepare_kernel(int* counter, float* dense, long long n_d
   if (dense) {
     for (long long j = i; j < n_dense; j += (long long)gridDim.x * blockDim.x) dense[j] = -__builtin_inff();
   }
+}
+
+// Ragged-batch item table (one workgroup of 1024 threads).
+__global__ void __launch_bounds__(1024) prefill_varlen_prepare_kernel(const int32_t* cu_q, const int32_t* cu_k,
+                                                                      int nseq, int total_q, int total_k, int rw,
+                                                                      int4* items, int cap_items, int* n_items,
+                                                                      int* counter) {
+  __shared__ int key[1024], idx[1024], scan[1024];
+  __shared__ int base;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    *counter = 0;
+    base = 0;
+  }
+  // query count, key count and items of sequence i (0 when its bounds are invalid)
+  auto seq = [&](int i, int& lq, int& lk) {
+    const int a = cu_q[i], b = cu_q[i + 1], c = cu_k[i], d = cu_k[i + 1];
+    const bool ok = 0 <= a && a <= b && b <= total_q && 0 <= c && c <= d && d <= total_k && b - a <= d - c;
+    lq = ok ? b - a : 0;
+    lk = ok ? d - c : 0;
+    return (lq + rw - 1) / rw;
+  };
+  auto block_scan = [&](int v) {   // inclusive prefix sum over the workgroup
+    scan[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int x = tid >= o ? scan[tid - o] : 0;
+      __syncthreads();
+      scan[tid] += x;
+      __syncthreads();
+    }
+    return scan[tid];
+  };
+  auto emit = [&](int i, int off) {   // items of sequence i, its longest first
+    int lq, lk;
+    const int nit = seq(i, lq, lk);
+    const int q0 = lk - lq;
+    for (int m = 0; m < nit && off + m < cap_items; ++m)
+      items[off + m] = make_int4(cu_q[i] - q0, cu_k[i], lk, q0 + (nit - 1 - m) * rw);
+  };
+  if (nseq <= 1024) {
+    // sequences by key count, descending (ties: lower index first), bitonic
+    int lq, lk;
+    key[tid] = tid < nseq ? (seq(tid, lq, lk), lk) : -1;
+    idx[tid] = tid;
+    __syncthreads();
+    for (int k = 2; k <= 1024; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const int pj = tid ^ j;
+        if (pj > tid) {
+          const bool up = (tid & k) == 0;
+          const bool partner_first = key[pj] > key[tid] || (key[pj] == key[tid] && idx[pj] < idx[tid]);
+          if (up == partner_first) {
+            const int tk = key[tid], ti = idx[tid];
+            key[tid] = key[pj];
+            idx[tid] = idx[pj];
+            key[pj] = tk;
+            idx[pj] = ti;
+          }
+        }
+        __syncthreads();
+      }
+    const int s = idx[tid];
+    const int nit = tid < nseq ? seq(s, lq, lk) : 0;
+    const int incl = block_scan(nit);
+    if (tid < nseq) emit(s, incl - nit);
+    if (tid == 1023) *n_items = min(incl, cap_items);
+  } else {
+    for (int c0 = 0; c0 < nseq; c0 += 1024) {
+      const int i = c0 + tid;
+      int lq, lk;
+      const int nit = i < nseq ? seq(i, lq, lk) : 0;
+      const int incl = block_scan(nit);
+      if (i < nseq) emit(i, base + incl - nit);
+      __syncthreads();
+      if (tid == 1023) base += incl;
+      __syncthreads();
+    }
+    if (tid == 0) *n_items = min(base, cap_items);
+  }
+}
+
+hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int nseq, int total_q, int total_k,
+                                  int rows_per_item, int4* items, int* n_items, int* counter, hipStream_t stream) {
+  const int cap_items = (total_q + rows_per_item - 1) / rows_per_item + nseq;
+  hipLaunchKernelGGL(prefill_varlen_prepare_kernel, dim3(1), dim3(1024), 0, stream, cu_q, cu_k, nseq, total_q,
+                     total_k, rows_per_item, items, cap_items, n_items, counter);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -128,19 +128,21 @@ def test_prefill_chunk_rejects_before_any_device_call():
 
 def test_prefill_varlen_rejects_before_any_device_call():
     lib = dsa.lib()
-    A = ctypes.c_int32 * 4
 
-    def call(cq=(0, 10, 20, 30), ck=(0, 10, 25, 40), n=3, H=64, wsb=1 << 30):
-        return lib.dsa_indexer_topk_prefill_varlen(FAKE, None, 0, FAKE, None, FAKE, A(*cq), A(*ck), n, H, 128, 16,
+    def call(n=3, tq=30, tk=40, H=64, wsb=1 << 30, cq=FAKE, q=FAKE):
+        return lib.dsa_indexer_topk_prefill_varlen(q, None, 0, FAKE, None, FAKE, cq, FAKE, n, tq, tk, H, 128, 16,
                                                    dsa.DSA_FP8_E4M3, FAKE, None, FAKE, wsb, None)
-    assert call(cq=(1, 10, 20, 30)) == dsa.DSA_ERR_INVALID_ARG          # does not start at 0
-    assert call(cq=(0, 10, 5, 30)) == dsa.DSA_ERR_INVALID_ARG           # decreasing
-    assert call(cq=(0, 11, 21, 31)) == dsa.DSA_ERR_INVALID_ARG          # more queries than keys
     assert call(n=0) == dsa.DSA_ERR_INVALID_ARG
+    assert call(tq=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert call(tk=-1) == dsa.DSA_ERR_INVALID_ARG
+    assert call(cq=None) == dsa.DSA_ERR_INVALID_ARG
+    assert call(q=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
     assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
-    n = dsa.dsa_indexer_topk_prefill_varlen_workspace([0, 10, 20, 30], [0, 10, 25, 40], 64, 128, 16, "fp8")
-    assert n == dsa.dsa_indexer_topk_prefill_workspace(10, 64, 128, 16, "fp8")
+    assert call(tq=0) == dsa.DSA_OK                    # nothing to select: nothing enqueued
+    n1 = dsa.dsa_indexer_topk_prefill_varlen_workspace(3, 30, 64, 128, 16, "fp8")
+    n2 = dsa.dsa_indexer_topk_prefill_varlen_workspace(3, 3000, 64, 128, 16, "fp8")
+    assert n2 > n1 > 0
 
 
 def test_decode_rejects_before_any_device_call():

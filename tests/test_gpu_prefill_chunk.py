@@ -90,44 +90,81 @@ def test_chunk_32k_tail_equals_whole_run(dsa):
 
 
 def test_varlen_batch_equals_per_sequence_calls(dsa):
-    """A packed ragged batch: whole sequences, chunks at the end of longer key
-    ranges, a one-token sequence and an empty query range; each sequence's
-    rows equal its own call byte for byte, and the oracle on sampled rows."""
+    """A packed ragged batch in one launch: whole sequences, chunks at the end
+    of longer key ranges, a one-token sequence, an empty query range and one
+    invalid sequence (more queries than keys, skipped: its rows keep their
+    bytes); each valid sequence's rows equal its own call byte for byte, and
+    the oracle on sampled rows."""
     import torch
     base = gen.CONFIGS["prefill_32k"]
     topk = 128
-    seqs = [(3000, 3000), (1200, 5003), (1, 1), (0, 700), (257, 257), (64, 2500)]   # (Lq, Lk)
+    seqs = [(3000, 3000), (1200, 5003), (1, 1), (0, 700), (257, 257), (64, 2500), (40, 20)]   # (Lq, Lk)
     parts = []
     for i, (lq, lk) in enumerate(seqs):
-        cfg = dict(base, L=lk, topk=topk, heavy_count=max(1, lk // 100), seed=10 + i)
+        cfg = dict(base, L=max(lq, lk), topk=topk, heavy_count=max(1, lk // 100), seed=10 + i)
         parts.append(gen.prefill_inputs(cfg))
-    rows_of = [np.arange(lk - lq, lk) for lq, lk in seqs]
+    rows_of = [np.arange(max(lk - lq, 0), max(lk - lq, 0) + lq) for lq, lk in seqs]
     cat = lambda key, sl: np.concatenate([p[key][sl(i)] for i, p in enumerate(parts)])
     q = cat("q", lambda i: rows_of[i])
     qs = cat("q_scale", lambda i: rows_of[i])
     w = cat("w", lambda i: rows_of[i])
-    k = cat("k", lambda i: slice(None))
-    ks = cat("k_scale", lambda i: slice(None))
-    cu_q = np.concatenate([[0], np.cumsum([lq for lq, _ in seqs])]).tolist()
-    cu_k = np.concatenate([[0], np.cumsum([lk for _, lk in seqs])]).tolist()
-    note("prefill varlen 6 sequences")
-    idx, sc = dsa.dsa_indexer_topk_prefill_varlen(dev(q), dev(qs), dev(k), dev(ks), dev(w), cu_q, cu_k, topk, "fp8",
-                                                  want_scores=True)
+    k = cat("k", lambda i: slice(0, seqs[i][1]))
+    ks = cat("k_scale", lambda i: slice(0, seqs[i][1]))
+    cu_q = np.concatenate([[0], np.cumsum([lq for lq, _ in seqs])]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum([lk for _, lk in seqs])]).astype(np.int32)
+    note("prefill varlen 7 sequences, one launch")
+    idx = torch.full((len(q), topk), -7, dtype=torch.int32, device="cuda")
+    idx, sc = dsa.dsa_indexer_topk_prefill_varlen(dev(q), dev(qs), dev(k), dev(ks), dev(w), dev(cu_q), dev(cu_k),
+                                                  topk, "fp8", out_idx=idx, want_scores=True)
     torch.cuda.synchronize()
     for i, (lq, lk) in enumerate(seqs):
         if lq == 0:
             continue
+        if lq > lk:
+            assert bool(torch.all(idx[cu_q[i]:cu_q[i + 1]] == -7)), i
+            continue
         p = parts[i]
         r = rows_of[i]
-        one, one_sc = dsa.dsa_indexer_topk_prefill_chunk(dev(p["q"][r]), dev(p["q_scale"][r]), dev(p["k"]),
-                                                         dev(p["k_scale"]), dev(p["w"][r]), lk - lq, topk, "fp8",
-                                                         want_scores=True)
+        one, one_sc = dsa.dsa_indexer_topk_prefill_chunk(dev(p["q"][r]), dev(p["q_scale"][r]), dev(p["k"][:lk]),
+                                                         dev(p["k_scale"][:lk]), dev(p["w"][r]), lk - lq, topk,
+                                                         "fp8", want_scores=True)
         torch.cuda.synchronize()
         assert torch.equal(idx[cu_q[i]:cu_q[i + 1]], one), i
         assert torch.equal(sc[cu_q[i]:cu_q[i + 1]], one_sc), i
         pick = np.unique(np.linspace(0, lq - 1, 6).astype(int))
-        res = oracle.prefill(p["q"][r][pick], p["q_scale"][r][pick], p["k"], p["k_scale"], p["w"][r][pick], "fp8",
-                             topk, rows=r[pick], return_scores=True)
+        res = oracle.prefill(p["q"][r][pick], p["q_scale"][r][pick], p["k"][:lk], p["k_scale"][:lk],
+                             p["w"][r][pick], "fp8", topk, rows=r[pick], return_scores=True)
         ih = host(idx[cu_q[i]:cu_q[i + 1]])
         for j, t in enumerate(pick):
             assert parity.check_row(ih[t], res["o"][j], res["A"][j], topk) is None, (i, t)
+
+
+def test_varlen_many_short_sequences_against_oracle(dsa):
+    """1100 sequences (more than the 1024 the table builder sorts), each of
+    1-40 keys with its last 1-3 rows as queries: every row against the oracle."""
+    import torch
+    rng = np.random.default_rng(42)
+    topk, H, D = 16, 64, 128
+    n = 1100
+    lk = rng.integers(1, 41, size=n)
+    lq = np.minimum(lk, rng.integers(1, 4, size=n))
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    K, kscale = gen.quant_rows_e4m3(rng.standard_normal((int(cu_k[-1]), D)).astype(np.float32))
+    Q, qscale = gen.quant_rows_e4m3(rng.standard_normal((int(cu_q[-1]), H * D)).astype(np.float32))
+    Q = Q.reshape(-1, H, D)
+    W = gen.bf16_bits((rng.standard_normal((int(cu_q[-1]), H)) / 8).astype(np.float32))
+    note("prefill varlen 1100 short sequences")
+    idx, sc = dsa.dsa_indexer_topk_prefill_varlen(dev(Q), dev(qscale), dev(K), dev(kscale), dev(W), dev(cu_q),
+                                                  dev(cu_k), topk, "fp8", want_scores=True)
+    torch.cuda.synchronize()
+    ih, sh = host(idx), host(sc)
+    for i in range(n):
+        q0 = int(lk[i] - lq[i])
+        rows = np.arange(q0, int(lk[i]))
+        sl = slice(int(cu_q[i]), int(cu_q[i + 1]))
+        res = oracle.prefill(Q[sl], qscale[sl], K[cu_k[i]:cu_k[i + 1]], kscale[cu_k[i]:cu_k[i + 1]], W[sl], "fp8",
+                             topk, rows=rows, return_scores=True)
+        for j in range(len(rows)):
+            g = int(cu_q[i]) + j
+            assert parity.check_row(ih[g], res["o"][j], res["A"][j], topk, g_score=sh[g]) is None, (i, j)
