@@ -168,3 +168,67 @@ def test_varlen_many_short_sequences_against_oracle(dsa):
         for j in range(len(rows)):
             g = int(cu_q[i]) + j
             assert parity.check_row(ih[g], res["o"][j], res["A"][j], topk, g_score=sh[g]) is None, (i, j)
+
+
+def test_prefill_and_ragged_graph_replays(dsa):
+    """The whole-sequence and the ragged-batch prefill captured in HIP graphs
+    (the work counter and the item table are written by kernels, no memset)
+    and replayed several times, with eager calls on other inputs between the
+    replays sharing the same workspace: every replay equals the eager result."""
+    import torch
+    base = gen.CONFIGS["prefill_32k"]
+    topk = 256
+    ca = dict(base, L=3000, topk=topk, heavy_count=30, seed=31)
+    cb = dict(base, L=2500, topk=topk, heavy_count=25, seed=32)
+    ia, ib = gen.prefill_inputs(ca), gen.prefill_inputs(cb)
+    da = {key: dev(ia[key]) for key in ("q", "q_scale", "k", "k_scale", "w")}
+    db = {key: dev(ib[key]) for key in ("q", "q_scale", "k", "k_scale", "w")}
+    ws = torch.full((dsa.dsa_indexer_topk_prefill_workspace(3000, 64, 128, topk, "fp8"),), 0x5A, dtype=torch.uint8,
+                    device="cuda")
+    note("prefill graph: eager references")
+    want_a, _, _ = dsa.dsa_indexer_topk_prefill(da["q"], da["q_scale"], da["k"], da["k_scale"], da["w"], topk, "fp8")
+    want_b, _, _ = dsa.dsa_indexer_topk_prefill(db["q"], db["q_scale"], db["k"], db["k_scale"], db["w"], topk, "fp8")
+    # ragged batch of the two sequences, the second one as its last 700 rows
+    q = torch.cat([da["q"], db["q"][-700:]])
+    qs = torch.cat([da["q_scale"], db["q_scale"][-700:]])
+    w = torch.cat([da["w"], db["w"][-700:]])
+    k = torch.cat([da["k"], db["k"]])
+    ks = torch.cat([da["k_scale"], db["k_scale"]])
+    cu_q = torch.tensor([0, 3000, 3700], dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0, 3000, 5500], dtype=torch.int32, device="cuda")
+    wsr = torch.full((dsa.dsa_indexer_topk_prefill_varlen_workspace(2, 3700, 64, 128, topk, "fp8"),), 0xFF,
+                     dtype=torch.uint8, device="cuda")
+    oa = torch.empty((3000, topk), dtype=torch.int32, device="cuda")
+    orr = torch.empty((3700, topk), dtype=torch.int32, device="cuda")
+
+    def whole():
+        dsa.dsa_indexer_topk_prefill(da["q"], da["q_scale"], da["k"], da["k_scale"], da["w"], topk, "fp8",
+                                     out_idx=oa, workspace=ws)
+
+    def ragged():
+        dsa.dsa_indexer_topk_prefill_varlen(q, qs, k, ks, w, cu_q, cu_k, topk, "fp8", out_idx=orr, workspace=wsr)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm-up on the capture stream
+        whole()
+        ragged()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        whole()
+    with torch.cuda.graph(g2):
+        ragged()
+    for rep in range(3):
+        note(f"prefill graph replay {rep}")
+        oa.fill_(-7)
+        orr.fill_(-7)
+        g1.replay()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oa, want_a), rep
+        assert torch.equal(orr[:3000], want_a) and torch.equal(orr[3000:], want_b[-700:]), rep
+        other, _, _ = dsa.dsa_indexer_topk_prefill(db["q"], db["q_scale"], db["k"], db["k_scale"], db["w"], topk,
+                                                   "fp8", workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, want_b), rep
