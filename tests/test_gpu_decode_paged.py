@@ -39,18 +39,19 @@ def _paginate(cache, k_scale, lens, page, seed, spare=3):
     return pages, spages, table
 
 
-@pytest.mark.parametrize("page", [32, 64, 256])
-def test_paged_equals_contiguous_and_oracle(dsa, page):
+@pytest.mark.parametrize("page,H,D", [(32, 64, 128), (64, 64, 128), (256, 64, 128), (64, 16, 64), (128, 32, 128),
+                                      (32, 64, 64)])
+def test_paged_equals_contiguous_and_oracle(dsa, page, H, D):
     import torch
-    B, Lmax, H, D, topk = 5, 4096, 64, 128, 256
-    rng = np.random.default_rng(page)
+    B, Lmax, topk = 5, 4096, 256
+    rng = np.random.default_rng(page + H + D)
     cache, ks = gen.quant_rows_e4m3(rng.standard_normal((B * Lmax, D)).astype(np.float32))
     cache, ks = cache.reshape(B, Lmax, D), ks.reshape(B, Lmax)
     q = gen.bf16_bits(rng.standard_normal((B, H, D)).astype(np.float32))
     w = gen.bf16_bits((rng.standard_normal((B, H)) / 8).astype(np.float32))
     lens = np.array([4096, 1, 200, 3001, 2048], dtype=np.int32)
     dc, dk, dq, dw, dl = dev(cache), dev(ks), dev(q), dev(w), dev(lens)
-    note(f"decode paged page={page}")
+    note(f"decode paged page={page} H={H} D={D}")
     idx_c, sc_c = dsa.dsa_indexer_topk_decode(dq, dw, dc, dk, dl, topk, want_scores=True)
     pages, spages, table = _paginate(dc, dk, dl, page, seed=page)
     idx_p, sc_p = dsa.dsa_indexer_topk_decode_paged(dq, dw, pages, spages, table, dl, topk, want_scores=True)

@@ -170,6 +170,50 @@ def test_varlen_many_short_sequences_against_oracle(dsa):
             assert parity.check_row(ih[g], res["o"][j], res["A"][j], topk, g_score=sh[g]) is None, (i, j)
 
 
+@pytest.mark.parametrize("dt,H,D", [("bf16", 16, 64), ("fp8", 8, 128), ("bf16", 32, 128)])
+def test_varlen_other_shapes_equal_per_sequence_calls(dsa, dt, H, D):
+    """The ragged batch for other built (dtype, H, D): per-head scales for fp8,
+    none for bf16; every sequence equals its own chunk call."""
+    import torch
+    rng = np.random.default_rng(H * D)
+    topk = 64
+    seqs = [(900, 900), (300, 1400), (1, 70), (65, 65)]
+    qs_all, ks_all = None, None
+    tq, tk = sum(a for a, _ in seqs), sum(b for _, b in seqs)
+    if dt == "bf16":
+        q = gen.bf16_bits((rng.standard_normal((tq, H, D)) / 8).astype(np.float32))
+        k = gen.bf16_bits((rng.standard_normal((tk, D)) / 8).astype(np.float32))
+    else:
+        q, qs_all = gen.quant_rows_e4m3(rng.standard_normal((tq * H, D)).astype(np.float32))
+        q, qs_all = q.reshape(tq, H, D), qs_all.reshape(tq, H)       # one scale per (token, head)
+        k, ks_all = gen.quant_rows_e4m3(rng.standard_normal((tk, D)).astype(np.float32))
+    w = gen.bf16_bits((rng.standard_normal((tq, H)) / 8).astype(np.float32))
+    cu_q = np.concatenate([[0], np.cumsum([a for a, _ in seqs])]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum([b for _, b in seqs])]).astype(np.int32)
+    stride = 1 if dt == "fp8" else 0
+    dq, dk, dw = dev(q), dev(k), dev(w)
+    dqs = dev(qs_all) if qs_all is not None else None
+    dks = dev(ks_all) if ks_all is not None else None
+    note(f"prefill varlen {dt} H={H} D={D}")
+    idx, sc = dsa.dsa_indexer_topk_prefill_varlen(dq, dqs, dk, dks, dw, dev(cu_q), dev(cu_k), topk, dt,
+                                                  q_scale_head_stride=stride, want_scores=True)
+    torch.cuda.synchronize()
+    for i, (lq, lk) in enumerate(seqs):
+        a, b, c, d = int(cu_q[i]), int(cu_q[i + 1]), int(cu_k[i]), int(cu_k[i + 1])
+        one, one_sc = dsa.dsa_indexer_topk_prefill_chunk(dq[a:b], dqs[a:b] if dqs is not None else None, dk[c:d],
+                                                         dks[c:d] if dks is not None else None, dw[a:b], lk - lq,
+                                                         topk, dt, q_scale_head_stride=stride, want_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(idx[a:b], one) and torch.equal(sc[a:b], one_sc), i
+        rows = np.arange(lk - lq, lk)
+        res = oracle.prefill(q[a:b], qs_all[a:b] if qs_all is not None else None, k[c:d],
+                             ks_all[c:d] if ks_all is not None else None, w[a:b], dt, topk, rows=rows,
+                             return_scores=True)
+        ih, sh = host(one), host(one_sc)
+        for j in range(0, lq, max(1, lq // 7)):
+            assert parity.check_row(ih[j], res["o"][j], res["A"][j], topk, g_score=sh[j]) is None, (i, j)
+
+
 def test_prefill_and_ragged_graph_replays(dsa):
     """The whole-sequence and the ragged-batch prefill captured in HIP graphs
     (the work counter and the item table are written by kernels, no memset)
