@@ -600,14 +600,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       size_t scr_bytes = (size_t)(scr_static_end - scr);
       if (reinterpret_cast<const uint8_t*>(dyn_lds) == scr_static_end)
         scr_bytes += (size_t)C::RW * p.sample_m * sizeof(float);
-      // The end of each share holds a 4-copy digit histogram when the share
-      // is large enough (lanes spread their atomics over the copies).
-      constexpr int HCOPIES = 4;
-      const int share = (int)(scr_bytes / WAVES / 16) * 4;   // floats per wave, a multiple of 4
-      const bool wide_hist = share >= 2 * 256 * HCOPIES;
-      const int lcap = wide_hist ? share - 256 * HCOPIES : share;
-      float* lbuf = reinterpret_cast<float*>(scr) + (size_t)wave * share;
-      uint32_t* fhist = reinterpret_cast<uint32_t*>(lbuf + lcap);
+      const int lcap = (int)(scr_bytes / WAVES / 16) * 4;   // floats per wave, a multiple of 4
+      float* lbuf = reinterpret_cast<float*>(scr) + (size_t)wave * lcap;
 #pragma unroll 1
       for (int rr = 0; rr < C::QPW; ++rr) {
         const int row = wave * C::QPW + rr;
@@ -615,12 +609,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         if (t >= L) continue;
         int* dix = p.out_idx + (size_t)(t + qoff) * p.topk;
         float* dsc = p.out_score ? p.out_score + (size_t)(t + qoff) * p.topk : nullptr;
-        if (wide_hist)
-          wave_select<HCOPIES>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc,
-                               dix, p.topk, fhist, nullptr, lbuf, lcap);
-        else
-          wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix,
-                      p.topk, sh.whist[wave], nullptr, lbuf, lcap);
+        wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix, p.topk,
+                    sh.whist[wave], nullptr, lbuf, lcap);
       }
       break;
     }
