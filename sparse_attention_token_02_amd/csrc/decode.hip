@@ -8,7 +8,7 @@
 // and the min(k, len_b) best keys (score descending, index ascending) are
 // written in ascending key order, padded with -1.
 //
-// Two launches:
+// Three launches:
 // 1. decode_score_kernel streams the fp8 cache once.  A wave reads 32 whole
 //    consecutive keys per step with 16-byte loads and keeps four steps in
 //    flight.  Each lane owns one key column and the D/2 contiguous bytes of
@@ -17,13 +17,19 @@
 //    on the MFMA row dimension (q stays in registers).  The per-token fp32
 //    scale multiplies the fp32 score (folding it into the bf16 operand would
 //    not be exact).  Scores go to a workspace row, and each workgroup stores
-//    its own 4096-bin histogram of the top 12 bits of their order-preserving
-//    keys (whole, so nothing has to be cleared beforehand).
-// 2. decode_select_kernel (one workgroup per sequence) sums those histograms,
-//    finds the bin of the k-th score, marks every key of a higher bin in an
-//    LDS bitmap and collects the keys of that bin as candidates in one pass
-//    over the scores, resolves the candidates by radix select (ties to the
-//    lower index), and writes the marked keys in ascending order.
+//    its own 16-bit histograms of its keys' order-preserving images: 4096
+//    fine bins (top 12 bits) and 256 coarse bins (top 8), written whole, so
+//    nothing has to be cleared beforehand.  With a paged cache (a block
+//    table of pages of 2^n >= 32 keys) each step lies in one page, whose id
+//    each wave looks up once per step at the start.
+// 2. decode_classify_kernel, several workgroups per sequence, each over a
+//    16384-key slice: sums the coarse then the fine partial histograms to the
+//    bin of the k-th score, marks the slice's keys of higher bins in a global
+//    bitmap and gathers the keys of that bin as candidates.
+// 3. decode_finalize_kernel, one workgroup per sequence: resolves the
+//    candidates by radix select (ties to the lower index), marks the kept
+//    ones and writes every marked key in ascending order.
+// The kernel boundaries order the phases (no cross-workgroup fences).
 #include "device_common.hpp"
 #include "kernels.hpp"
 

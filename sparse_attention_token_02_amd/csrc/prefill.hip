@@ -44,6 +44,11 @@
 //   row and writes them out in order.
 // * Persistent grid: one workgroup per CU pulls work items from an atomic
 //   counter, longest (highest t) first, which balances the causal triangle.
+// * Query rows need not start at position 0: a chunk (query offset q0) or a
+//   ragged batch (a device table of items, each naming its sequence's key
+//   rows, key count, q row offset and first position) reads its rows at
+//   t + offset and its keys from its own sequence; positions, tiles and the
+//   causal mask stay absolute.
 #include "device_common.hpp"
 #include "wave_select.hpp"
 #include "kernels.hpp"
