@@ -252,7 +252,7 @@ struct EventSet {
   hipEvent_t ev[4] = {};
   int n = 0;
   ~EventSet() {
-    for (int i = 0; i < n; ++i) hipEventDestroy(ev[i]);
+    for (int i = 0; i < n; ++i) (void)hipEventDestroy(ev[i]);
   }
   hipError_t create(int count, unsigned flags) {
     for (; n < count; ++n) {

@@ -424,8 +424,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       // key tiles below t0 (valid for every row of the item) into LDS; their
       // scores give a conservative estimate tau0 of each row's k-th score.
       // The remaining iterations stream the causal prefix in key order.
-      const int smp_tiles = (attempt == 0 && t0 >= 4 * p.topk) ? min(p.sample_m / C::TK, t0 / (8 * C::TK)) : 0;
-      const int stile = smp_tiles >= 4 ? smp_tiles : 0;
+      // (from t0 >= 3k: there a sample of at least 2 tiles already gives a
+      // threshold that keeps the lists, and the end-of-item selection, short)
+      const int smp_tiles = (attempt == 0 && t0 >= 3 * p.topk) ? min(p.sample_m / C::TK, t0 / (8 * C::TK)) : 0;
+      const int stile = smp_tiles >= 2 ? smp_tiles : 0;
       const int stride = stile ? (t0 / stile) / C::TK * C::TK : 0;
       const int total = stile + ntiles;
       auto tile_key = [&](int i) { return i < stile ? i * stride : (i - stile) * C::TK; };
