@@ -1,6 +1,9 @@
 // Wave-level (64-lane) selection for gfx950: exact k-th largest key of a set
 // of floats and exact top-k of a candidate list, each run by one wave with
-// a 256-bin histogram in LDS and no workgroup barrier.
+// a 256-bin histogram in LDS and no workgroup barrier.  Everything is
+// inlined: as called functions these took generic pointers, so the
+// histogram updates became FLAT atomics and every call saved registers to
+// scratch.
 //
 // Keys: order-preserving 32-bit images of the scores (ordered_key), so a
 // radix select over key bits, most significant first, finds the k-th score
@@ -99,7 +102,7 @@ struct WaveCut {
 // pass when need_kth (else kth is left 0).  `hist` is 256 words of this
 // wave's LDS.  lo_hi, when given, holds the smallest and largest key
 // (reduced over the wave), which saves the first pass.
-__device__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist, bool need_kth = true,
+__device__ __forceinline__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist, bool need_kth = true,
                                  const uint32_t* lo_hi = nullptr) {
   const int lane = __lane_id();
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -181,7 +184,7 @@ __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int k
 // lbuf (16-byte aligned wave-private LDS of lcap floats, lcap a multiple of
 // 4, or null): when the list fits, its scores are copied there once and every
 // later pass reads them from LDS (then dsc must not alias sc).
-__device__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
+__device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
                            uint32_t* hist, float* tau, float* lbuf = nullptr, int lcap = 0) {
   const int lane = __lane_id();
   WaveCut cut{0u, 0u, 0xFFFFFFFFu, 0u};   // keeps everything
