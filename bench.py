@@ -175,6 +175,9 @@ def run_main(args):
         ev.append(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    # decode on its own (outside the timed steps): back to back, alternating
+    # the two cache copies, with no prefill writing back its lines in between
+    alone = time_calls(decode, max(5, args.steps), 2, stream)
     pf_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
     dc_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
     med = lambda xs: xs[len(xs) // 2]
@@ -205,6 +208,7 @@ def run_main(args):
         "prefill_ms": round(pf_avg, 4), "prefill_ms_median": round(med(pf_ms), 4),
         "prefill_rows_per_s": round(L / (pf_avg * 1e-3), 1),
         "decode_us": round(dc_avg * 1e3, 2), "decode_us_median": round(med(dc_ms) * 1e3, 2),
+        "decode_alone_us": round(sum(alone) / len(alone) * 1e3, 2),
         "decode_GBps": round(dc_gbps, 1),
         "decode_rows_per_s": round(B / (dc_avg * 1e-3), 1),
         "roofline": {"bound": "mfma", "achieved": round(pf_tflops, 2), "peak": PEAK_FP8_TFLOPS,
