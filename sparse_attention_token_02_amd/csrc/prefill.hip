@@ -607,8 +607,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       size_t scr_bytes = (size_t)(scr_static_end - scr);
       if (reinterpret_cast<const uint8_t*>(dyn_lds) == scr_static_end)
         scr_bytes += (size_t)C::RW * p.sample_m * sizeof(float);
-      const int lcap = (int)(scr_bytes / WAVES / 16) * 4;   // floats per wave, a multiple of 4
-      float* lbuf = reinterpret_cast<float*>(scr) + (size_t)wave * lcap;
+      // A row whose list leaves room in the share for a 4-copy digit
+      // histogram gets one at the end of the share; a longer list keeps the
+      // whole share for its scores and counts into the wave's 1-copy one.
+      constexpr int HCOPIES = 4;
+      const int share = (int)(scr_bytes / WAVES / 16) * 4;   // floats per wave, a multiple of 4
+      const int lcap_w = share - 256 * HCOPIES;
+      float* lbuf = reinterpret_cast<float*>(scr) + (size_t)wave * share;
+      uint32_t* fhist = reinterpret_cast<uint32_t*>(lbuf + (lcap_w > 0 ? lcap_w : 0));
 #pragma unroll 1
       for (int rr = 0; rr < C::QPW; ++rr) {
         const int row = wave * C::QPW + rr;
@@ -616,8 +622,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         if (t >= L) continue;
         int* dix = p.out_idx + (size_t)(t + qoff) * p.topk;
         float* dsc = p.out_score ? p.out_score + (size_t)(t + qoff) * p.topk : nullptr;
-        wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, sh.row_cnt[row], p.topk, dsc, dix, p.topk,
-                    sh.whist[wave], nullptr, lbuf, lcap);
+        const int n = sh.row_cnt[row];
+        if (n <= lcap_w)
+          wave_select<HCOPIES>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, n, p.topk, dsc, dix, p.topk,
+                               fhist, nullptr, lbuf, lcap_w);
+        else
+          wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, n, p.topk, dsc, dix, p.topk,
+                      sh.whist[wave], nullptr, lbuf, share);
       }
       break;
     }

@@ -29,16 +29,21 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Boundary digit of a 256-bin histogram whose bins are indexed by digit
 // value (larger digit = larger key), 4 bins per lane (lane l: 4l..4l+3).
+// With COPIES > 1 the histogram is COPIES interleaved partial counts, bin b
+// copy c at word COPIES * b + c (summed here).
 // Returns d such that the bins above d hold fewer than `need` entries and
 // bins d and above hold at least `need` (requires 1 <= need <= total).
 // *above = entries in bins above d, *count = entries in bin d.
+template <int COPIES = 1>
 __device__ __forceinline__ int wave_boundary_digit(const uint32_t* hist, uint32_t need, uint32_t* above,
                                                    uint32_t* count) {
   const int lane = __lane_id();
   uint32_t h[4], sum = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    h[b] = hist[4 * lane + b];
+    h[b] = 0;
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c) h[b] += hist[COPIES * (4 * lane + b) + c];
     sum += h[b];
   }
   // entries in the bins of this lane and all higher lanes
@@ -99,9 +104,13 @@ struct WaveCut {
 // Radix search for the cut that keeps exactly k of the n keys of vals[0..n)
 // (requires n > k >= 1).  Stops as soon as the boundary bin is kept whole;
 // the k-th key is then the smallest key of that bin, found with one more
-// pass when need_kth (else kth is left 0).  `hist` is 256 words of this
-// wave's LDS.  lo_hi, when given, holds the smallest and largest key
-// (reduced over the wave), which saves the first pass.
+// pass when need_kth (else kth is left 0).  `hist` is COPIES * 256 words of
+// this wave's LDS: lane l counts into copy l % COPIES, the copies of a bin
+// adjacent, so lanes that hit the same bin at once (scores sharing their
+// leading bits) spread over COPIES addresses in different banks.  lo_hi,
+// when given, holds the smallest and largest key (reduced over the wave),
+// which saves the first pass.
+template <int COPIES = 1>
 __device__ __forceinline__ WaveCut wave_find_cut(const float* vals, int n, int k, uint32_t* hist, bool need_kth = true,
                                  const uint32_t* lo_hi = nullptr) {
   const int lane = __lane_id();
@@ -130,14 +139,14 @@ __device__ __forceinline__ WaveCut wave_find_cut(const float* vals, int n, int k
     const int shift = bit + 1 - nb;
     const uint32_t dm = (1u << nb) - 1u;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
+    for (int b = 0; b < 4 * COPIES; ++b) hist[64 * b + lane] = 0u;
     wave_lds_sync();
     wave_for_score_keys(vals, n, [&](uint32_t key) {
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dm], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&hist[COPIES * ((key >> shift) & dm) + (lane & (COPIES - 1))], 1u);
     });
     wave_lds_sync();
     uint32_t above, count;
-    const int d = wave_boundary_digit(hist, need, &above, &count);
+    const int d = wave_boundary_digit<COPIES>(hist, need, &above, &count);
     wave_lds_sync();   // every lane has read the histogram before it is cleared again
     need -= above;
     prefix |= (uint32_t)d << shift;
@@ -184,6 +193,8 @@ __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int k
 // lbuf (16-byte aligned wave-private LDS of lcap floats, lcap a multiple of
 // 4, or null): when the list fits, its scores are copied there once and every
 // later pass reads them from LDS (then dsc must not alias sc).
+// hist: COPIES * 256 words (see wave_find_cut).
+template <int COPIES = 1>
 __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
                            uint32_t* hist, float* tau, float* lbuf = nullptr, int lcap = 0) {
   const int lane = __lane_id();
@@ -221,7 +232,7 @@ __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n
     wave_lds_sync();
     ksc = lbuf;
   }
-  if (n > k) cut = wave_find_cut(ksc, n, k, hist, tau != nullptr, have_lo_hi ? lo_hi : nullptr);
+  if (n > k) cut = wave_find_cut<COPIES>(ksc, n, k, hist, tau != nullptr, have_lo_hi ? lo_hi : nullptr);
   if (tau) *tau = n > k ? key_to_float(cut.kth) : -__builtin_inff();
   int out = 0;
   uint32_t eq_seen = 0;
