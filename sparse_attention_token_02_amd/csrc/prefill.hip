@@ -425,8 +425,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       // scores give a conservative estimate tau0 of each row's k-th score.
       // The remaining iterations stream the causal prefix in key order.
       // (from t0 >= 3k: there a sample of at least 2 tiles already gives a
-      // threshold that keeps the lists, and the end-of-item selection, short)
-      const int smp_tiles = (attempt == 0 && t0 >= 3 * p.topk) ? min(p.sample_m / C::TK, t0 / (8 * C::TK)) : 0;
+      // threshold that keeps the lists, and the end-of-item selection, short).
+      // The sample grows with the prefix, one tile per 64 tiles of keys
+      // beyond the first two (and at most 1/8 of the keys, at most sample_m):
+      // a short row gains less from a tighter threshold than the extra
+      // sample tiles cost it.
+      const int smp_tiles = (attempt == 0 && t0 >= 3 * p.topk)
+                                ? min(min(p.sample_m / C::TK, t0 / (8 * C::TK)), max(2, t0 / (64 * C::TK)))
+                                : 0;
       const int stile = smp_tiles >= 2 ? smp_tiles : 0;
       const int stride = stile ? (t0 / stile) / C::TK * C::TK : 0;
       const int total = stile + ntiles;
