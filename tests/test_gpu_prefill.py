@@ -189,6 +189,24 @@ def test_every_built_configuration(dsa, dt, H, D):
     _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
 
 
+@pytest.mark.parametrize("dt,H,D", BUILT)
+def test_every_built_configuration_with_key_sample(dsa, dt, H, D):
+    """L=5003, k=64: work items from position 2048 (128-key tiles) or 4096
+    (256-key tiles) on score a key sample first and filter with its
+    threshold, so this covers the sample path of every layout (the query
+    slots of H <= 16 included), not only the benchmark's."""
+    L, topk = 5003, 64
+    cfg = dict(kind="prefill", L=L, H=H, D=D, topk=topk, dtype=dt, seed=3 * H + D + (dt == "bf16"),
+               heavy_count=L // 100, heavy_factor=3.0, qk_div=8.0, w_div=8.0)
+    note(f"prefill configuration with key sample {dt} H={H} D={D} L={L} k={topk}")
+    inp = gen.prefill_inputs(cfg)
+    idx, sc, _ = _run(dsa, inp, cfg, want_scores=True)
+    check_structure_all(idx, topk)
+    around = {2047, 2048, 2049, 2055, 2056, 4095, 4096, 4097, 4103, 4104}
+    rows = np.array(sorted(set(sample_rows(L, topk, 20, seed=H + D).tolist()) | around), dtype=np.int64)
+    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
+
+
 @pytest.mark.parametrize("L,topk", [(700, 1), (5003, 4096)])
 def test_topk_limits(dsa, L, topk):
     """The smallest k and the largest the library accepts."""
