@@ -426,10 +426,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       // The remaining iterations stream the causal prefix in key order.
       // (from t0 >= 3k: there a sample of at least 2 tiles already gives a
       // threshold that keeps the lists, and the end-of-item selection, short).
-      // The sample grows with the prefix, one tile per 64 tiles of keys
-      // beyond the first two (and at most 1/8 of the keys, at most sample_m):
-      // a short row gains less from a tighter threshold than the extra
-      // sample tiles cost it.
+      // The sample grows with the prefix: one tile per 64 tiles of keys, at
+      // least two, at most 1/8 of the keys and at most sample_m keys.  A
+      // short row gains less from a tighter threshold than extra sample
+      // tiles cost it.
       const int smp_tiles = (attempt == 0 && t0 >= 3 * p.topk)
                                 ? min(min(p.sample_m / C::TK, t0 / (8 * C::TK)), max(2, t0 / (64 * C::TK)))
                                 : 0;
