@@ -11,11 +11,15 @@
 // A workgroup handles a strided subset of the rows.  The key range of a row,
 // [0, largest index any layer holds in it] (at most [0, t] for a causal
 // prefill row, [0, len_b) for a decode row), is cut into windows of 8192
-// keys; for each window every layer's keys
-// are set in an LDS bitmap (the range of each sorted list that falls in the
-// window is found by binary search), then every thread ANDs and popcounts the
-// bitmaps of its layer pairs and keeps the running counts in registers until
-// the workgroup is done.
+// keys; for each window every layer's keys are set in an LDS bitmap, then
+// every thread ANDs and popcounts the bitmaps of its layer pairs (16 bytes
+// per read) and keeps the running counts in registers until the workgroup is
+// done.  The part of each sorted list that falls in a window starts where the
+// previous window's part ended, so one binary search per layer and window
+// finds it; each wave fills the bitmaps of its own layers with 16 loads in
+// flight per lane.  Bitmap rows are padded so that consecutive layers start 4
+// banks apart: lanes reading the same word of different layers do not
+// collide.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +29,8 @@ namespace {
 constexpr int OV_NT = 256;
 constexpr int OV_WBITS = 8192;
 constexpr int OV_WWORDS = OV_WBITS / 32;
+constexpr int OV_RS = OV_WWORDS + 4;   // LDS words per layer bitmap row (16-byte aligned, 4 banks apart)
+constexpr int OV_U = 16;               // index loads in flight per lane while filling
 constexpr int OV_PPT = (OVERLAP_MAX_N * (OVERLAP_MAX_N + 1) / 2 + OV_NT - 1) / OV_NT;  // pairs per thread
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
@@ -39,9 +45,9 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
 }  // namespace
 
 __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
-  extern __shared__ uint32_t bms[];          // [N][OV_WWORDS]
+  extern __shared__ __attribute__((aligned(16))) uint32_t bms[];   // [N][OV_RS]
   __shared__ int rng_lo[OVERLAP_MAX_N], rng_hi[OVERLAP_MAX_N], valid_n[OVERLAP_MAX_N], last_key[OVERLAP_MAX_N];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = p.N;
   const int P = N * (N + 1) / 2;
 
@@ -68,10 +74,12 @@ __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
   for (long long ri = blockIdx.x; ri < nrows; ri += gridDim.x) {
     const int t = (int)(p.row_begin + ri * p.row_stride);
     // number of valid (non-negative) entries of each layer's row: the -1
-    // padding sits at the tail, so a binary search finds it
+    // padding sits at the tail, so a binary search finds it (a full row
+    // needs only its last entry)
     if (tid < N) {
       const int32_t* row = p.idx[tid] + (size_t)t * p.topk;
       int lo = 0, hi = p.topk;
+      if (row[p.topk - 1] >= 0) lo = p.topk;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (row[mid] >= 0) lo = mid + 1;
@@ -88,19 +96,26 @@ __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
     const int nwin = (kmax + OV_WBITS) / OV_WBITS;   // windows covering [0, kmax]
     for (int win = 0; win < nwin; ++win) {
       const int v0 = win * OV_WBITS;
-      for (int i = tid; i < N * OV_WWORDS; i += OV_NT) bms[i] = 0u;
-      if (tid < N) {
+      for (int i = tid; i < N * OV_RS / 4; i += OV_NT) reinterpret_cast<v4i*>(bms)[i] = v4i{0, 0, 0, 0};
+      if (tid < N) {   // each thread owns its layer's entry: no race with the previous window
         const int32_t* row = p.idx[tid] + (size_t)t * p.topk;
-        rng_lo[tid] = lower_bound_i32(row, valid_n[tid], v0);
+        rng_lo[tid] = win == 0 ? 0 : rng_hi[tid];
         rng_hi[tid] = lower_bound_i32(row, valid_n[tid], v0 + OV_WBITS);
       }
       __syncthreads();
-      for (int i = 0; i < N; ++i) {
+      for (int i = wave; i < N; i += OV_NT / 64) {
         const int32_t* row = p.idx[i] + (size_t)t * p.topk;
         const int lo = rng_lo[i], hi = rng_hi[i];
-        for (int e = lo + tid; e < hi; e += OV_NT) {
-          const int v = row[e] - v0;
-          if (v >= 0 && v < OV_WBITS) atomicOr(&bms[i * OV_WWORDS + (v >> 5)], 1u << (v & 31));
+        uint32_t* bm = bms + i * OV_RS;
+        for (int e0 = lo + lane; e0 < hi; e0 += 64 * OV_U) {
+          int v[OV_U];
+#pragma unroll
+          for (int u = 0; u < OV_U; ++u) v[u] = row[min(e0 + 64 * u, hi - 1)];
+#pragma unroll
+          for (int u = 0; u < OV_U; ++u) {
+            const int x = v[u] - v0;
+            if (e0 + 64 * u < hi && x >= 0 && x < OV_WBITS) atomicOr(&bm[x >> 5], 1u << (x & 31));
+          }
         }
       }
       __syncthreads();
@@ -108,10 +123,16 @@ __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
 #pragma unroll
       for (int u = 0; u < OV_PPT; ++u) {
         if (pi[u] >= 0) {
-          const uint32_t* a = bms + pi[u] * OV_WWORDS;
-          const uint32_t* c = bms + pj[u] * OV_WWORDS;
+          // whole 16-byte groups: words past nwords hold keys above every
+          // layer's largest and are zero
+          const v4i* a = reinterpret_cast<const v4i*>(bms + pi[u] * OV_RS);
+          const v4i* c = reinterpret_cast<const v4i*>(bms + pj[u] * OV_RS);
           unsigned s = 0;
-          for (int wd = 0; wd < nwords; ++wd) s += __popc(a[wd] & c[wd]);
+          for (int q = 0; q < (nwords + 3) >> 2; ++q) {
+            const v4i x = a[q], y = c[q];
+            s += __popc((uint32_t)(x[0] & y[0])) + __popc((uint32_t)(x[1] & y[1])) + __popc((uint32_t)(x[2] & y[2])) +
+                 __popc((uint32_t)(x[3] & y[3]));
+          }
           acc[u] += s;
         }
       }
@@ -131,11 +152,15 @@ __global__ void overlap_prepare_kernel(unsigned long long* counts, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) counts[i] = 0ull;
 }
 
-size_t overlap_lds_bytes(int N) { return (size_t)N * OV_WWORDS * sizeof(uint32_t); }
+size_t overlap_lds_bytes(int N) { return (size_t)N * OV_RS * sizeof(uint32_t); }
 
 hipError_t overlap_launch(const OverlapParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(overlap_prepare_kernel, dim3(1), dim3(256), 0, stream, p.counts, p.N * p.N);
-  hipLaunchKernelGGL(overlap_kernel, dim3(grid), dim3(OV_NT), overlap_lds_bytes(p.N), stream, p);
+  const size_t lds = overlap_lds_bytes(p.N);   // above 64 KB for N = 64
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&overlap_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(overlap_kernel, dim3(grid), dim3(OV_NT), lds, stream, p);
   return hipGetLastError();
 }
 

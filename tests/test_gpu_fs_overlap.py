@@ -29,7 +29,8 @@ def _random_sets(N, L, k, seed):
     return out
 
 
-@pytest.mark.parametrize("N,L,k,rows", [(6, 700, 64, None), (47, 1400, 1024, None), (8, 2400, 2048, None), (5, 900, 32, (10, 900, 7))])
+@pytest.mark.parametrize("N,L,k,rows", [(6, 700, 64, None), (47, 1400, 1024, None), (8, 2400, 2048, None), (5, 900, 32, (10, 900, 7)),
+                                        (64, 600, 48, None)])
 def test_overlap_matches_oracle_exactly(dsa, N, L, k, rows):
     import torch
     sets = _random_sets(N, L, k, seed=N)
