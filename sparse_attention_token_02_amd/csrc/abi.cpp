@@ -719,7 +719,7 @@ dsa_status topk_overlap_matrix(const int32_t* const* idx, int N, int L, int topk
   int cus = 0;
   if (device_cus(&cus) != 0) return fail(DSA_ERR_HIP, "no HIP device");
   const long long nrows = (row_end - row_begin + row_stride - 1) / row_stride;
-  long long grid = 4LL * cus;
+  long long grid = (long long)dsa::overlap_blocks_per_cu(N) * cus;   // one pass of resident workgroups
   if (grid > nrows) grid = nrows;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = dsa::overlap_launch(p, (int)grid, s);

@@ -129,6 +129,7 @@ hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream
 
 // overlap.hip
 size_t overlap_lds_bytes(int N);
+int overlap_blocks_per_cu(int N);
 hipError_t overlap_launch(const OverlapParams& p, int grid, hipStream_t stream);
 
 }  // namespace dsa

@@ -14,10 +14,10 @@
 // keys; for each window every layer's keys are set in an LDS bitmap, then
 // every thread ANDs and popcounts the bitmaps of its layer pairs (16 bytes
 // per read) and keeps the running counts in registers until the workgroup is
-// done.  The part of each sorted list that falls in a window starts where the
-// previous window's part ended, so one binary search per layer and window
-// finds it; each wave fills the bitmaps of its own layers with 16 loads in
-// flight per lane.  Bitmap rows are padded so that consecutive layers start 4
+// done.  The boundaries of each sorted list between windows are found up
+// front, all at once (or, for rows of very many windows, one search per
+// layer and window, each window starting where the previous one ended); each wave fills the bitmaps of its own layers, four at a time
+// with 16 loads per lane and layer in flight.  Bitmap rows are padded so that consecutive layers start 4
 // banks apart: lanes reading the same word of different layers do not
 // collide.
 #include "device_common.hpp"
@@ -30,7 +30,9 @@ constexpr int OV_NT = 256;
 constexpr int OV_WBITS = 8192;
 constexpr int OV_WWORDS = OV_WBITS / 32;
 constexpr int OV_RS = OV_WWORDS + 4;   // LDS words per layer bitmap row (16-byte aligned, 4 banks apart)
-constexpr int OV_U = 16;               // index loads in flight per lane while filling
+constexpr int OV_U = 16;               // index loads per lane and layer in one fill batch
+constexpr int OV_G = 4;                // layers a wave fills together
+constexpr int OV_MAXW = 16;            // rows of at most this many windows get all boundaries up front
 constexpr int OV_PPT = (OVERLAP_MAX_N * (OVERLAP_MAX_N + 1) / 2 + OV_NT - 1) / OV_NT;  // pairs per thread
 
 __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
@@ -47,6 +49,7 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int v) {
 __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
   extern __shared__ __attribute__((aligned(16))) uint32_t bms[];   // [N][OV_RS]
   __shared__ int rng_lo[OVERLAP_MAX_N], rng_hi[OVERLAP_MAX_N], valid_n[OVERLAP_MAX_N], last_key[OVERLAP_MAX_N];
+  __shared__ int bnd[OVERLAP_MAX_N][OV_MAXW + 1];   // bnd[i][w]: first entry of layer i in window w
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int N = p.N;
   const int P = N * (N + 1) / 2;
@@ -94,28 +97,59 @@ __global__ void __launch_bounds__(OV_NT) overlap_kernel(OverlapParams p) {
     kmax = min(kmax, OVERLAP_MAX_KEY);
     __syncthreads();   // every thread has read last_key before the next row rewrites it
     const int nwin = (kmax + OV_WBITS) / OV_WBITS;   // windows covering [0, kmax]
+    // Up to OV_MAXW windows: every boundary of every layer at once, as
+    // independent searches spread over the workgroup (read after the first
+    // window's barrier).  Longer rows search one boundary per window.
+    const bool pre = nwin <= OV_MAXW;
+    if (pre) {
+      for (int q = tid; q < N * (nwin - 1); q += OV_NT) {
+        const int i = q / (nwin - 1), w = 1 + q % (nwin - 1);
+        bnd[i][w] = lower_bound_i32(p.idx[i] + (size_t)t * p.topk, valid_n[i], w * OV_WBITS);
+      }
+      if (tid < N) {
+        bnd[tid][0] = 0;
+        bnd[tid][nwin] = valid_n[tid];
+      }
+    }
     for (int win = 0; win < nwin; ++win) {
       const int v0 = win * OV_WBITS;
       for (int i = tid; i < N * OV_RS / 4; i += OV_NT) reinterpret_cast<v4i*>(bms)[i] = v4i{0, 0, 0, 0};
-      if (tid < N) {   // each thread owns its layer's entry: no race with the previous window
+      if (!pre && tid < N) {   // each thread owns its layer's entry: no race with the previous window
         const int32_t* row = p.idx[tid] + (size_t)t * p.topk;
         rng_lo[tid] = win == 0 ? 0 : rng_hi[tid];
         rng_hi[tid] = lower_bound_i32(row, valid_n[tid], v0 + OV_WBITS);
       }
       __syncthreads();
-      for (int i = wave; i < N; i += OV_NT / 64) {
-        const int32_t* row = p.idx[i] + (size_t)t * p.topk;
-        const int lo = rng_lo[i], hi = rng_hi[i];
-        uint32_t* bm = bms + i * OV_RS;
-        for (int e0 = lo + lane; e0 < hi; e0 += 64 * OV_U) {
-          int v[OV_U];
+      // wave w fills layers w, w + 4, ..., OV_G of them at a time, so that
+      // OV_G * OV_U index loads per lane are in flight together
+      constexpr int NW = OV_NT / 64;
+      for (int i0 = wave; i0 < N; i0 += OV_G * NW) {
+        const int32_t* row[OV_G];
+        int lo[OV_G], hi[OV_G];
+        int nb = 0;   // batches of the group's longest range (wave-uniform)
 #pragma unroll
-          for (int u = 0; u < OV_U; ++u) v[u] = row[min(e0 + 64 * u, hi - 1)];
+        for (int g = 0; g < OV_G; ++g) {
+          const int i = i0 + g * NW;
+          row[g] = p.idx[i < N ? i : 0] + (size_t)t * p.topk;
+          lo[g] = i < N ? (pre ? bnd[i][win] : rng_lo[i]) : 0;
+          hi[g] = i < N ? (pre ? bnd[i][win + 1] : rng_hi[i]) : 0;
+          nb = max(nb, (hi[g] - lo[g] + 64 * OV_U - 1) / (64 * OV_U));
+        }
+        for (int bt = 0; bt < nb; ++bt) {
+          int v[OV_G][OV_U];
 #pragma unroll
-          for (int u = 0; u < OV_U; ++u) {
-            const int x = v[u] - v0;
-            if (e0 + 64 * u < hi && x >= 0 && x < OV_WBITS) atomicOr(&bm[x >> 5], 1u << (x & 31));
-          }
+          for (int g = 0; g < OV_G; ++g)
+#pragma unroll
+            for (int u = 0; u < OV_U; ++u)   // clamped into [0, hi): in bounds, unused past hi
+              v[g][u] = row[g][max(min(lo[g] + 64 * (bt * OV_U + u) + lane, hi[g] - 1), 0)];
+#pragma unroll
+          for (int g = 0; g < OV_G; ++g)
+#pragma unroll
+            for (int u = 0; u < OV_U; ++u) {
+              const int x = v[g][u] - v0;
+              if (lo[g] + 64 * (bt * OV_U + u) + lane < hi[g] && x >= 0 && x < OV_WBITS)
+                atomicOr(&bms[(i0 + g * NW) * OV_RS + (x >> 5)], 1u << (x & 31));
+            }
         }
       }
       __syncthreads();
@@ -153,6 +187,19 @@ __global__ void overlap_prepare_kernel(unsigned long long* counts, int n) {
 }
 
 size_t overlap_lds_bytes(int N) { return (size_t)N * OV_RS * sizeof(uint32_t); }
+
+// Workgroups of the overlap kernel resident on one CU with N layers (at least
+// 1): the grid is sized to this times the CU count, so that no workgroup
+// waits for a second pass that would run with fewer neighbours to hide its
+// load latency.
+int overlap_blocks_per_cu(int N) {
+  const size_t lds = overlap_lds_bytes(N);
+  const void* fn = reinterpret_cast<const void*>(&overlap_kernel);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) return 1;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, OV_NT, lds) != hipSuccess || nb < 1) return 1;
+  return nb;
+}
 
 hipError_t overlap_launch(const OverlapParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(overlap_prepare_kernel, dim3(1), dim3(256), 0, stream, p.counts, p.N * p.N);

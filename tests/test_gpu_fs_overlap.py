@@ -50,15 +50,18 @@ def test_overlap_matches_oracle_exactly(dsa, N, L, k, rows):
         assert ratio[1, 2] == ratio[1, 1]
 
 
-def test_overlap_of_decode_rows_matches_oracle(dsa):
+@pytest.mark.parametrize("kmax", [131072, 400000])
+def test_overlap_of_decode_rows_matches_oracle(dsa, kmax):
     """Decode-shaped rows: one row per sequence, keys far beyond the row
-    number (up to 131071), short rows padded with -1, one empty row."""
+    number (below kmax), short rows padded with -1, one empty row.  Rows of
+    up to 16 windows of 8192 keys get their window boundaries up front, longer
+    ones (kmax = 400000) one search per window."""
     import torch
     rng = np.random.default_rng(5)
     N, R, k = 7, 40, 512
     sets = np.full((N, R, k), -1, dtype=np.int32)
     for b in range(R - 1):
-        n = int(rng.integers(k // 2, 131072))
+        n = int(rng.integers(k // 2, kmax))
         base = np.sort(rng.choice(n, size=min(k, n), replace=False))
         for i in range(N):
             keep = base.copy()
@@ -66,7 +69,7 @@ def test_overlap_of_decode_rows_matches_oracle(dsa):
             keep[swap] = rng.choice(n, size=int(swap.sum()), replace=True)
             keep = np.unique(keep)[:k]
             sets[i, b, :len(keep)] = keep
-    note("overlap decode rows N=7 R=40 k=512")
+    note(f"overlap decode rows N=7 R=40 k=512 kmax={kmax}")
     counts, ratio = dsa.topk_overlap_matrix([dev(sets[i]) for i in range(N)], k, row_begin=0, row_end=R)
     torch.cuda.synchronize()
     want = oracle.overlap_counts([sets[i] for i in range(N)], range(R))
