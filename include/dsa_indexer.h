@@ -92,7 +92,10 @@ dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa
  * w        [L, H] bf16           head weights
  * L >= 1; H in {8, 16, 32, 64}; D in {64, 128} (bf16: not H=64 with D=128);
  * 1 <= topk <= 4096.
- * out_idx        [L, topk] int32  selected keys, ascending, -1 padded (written in full)
+ * out_idx        [L, topk] int32  selected keys, ascending, -1 padded (written in full).
+ *                A key whose score is NaN or -inf (finite but extreme inputs can
+ *                overflow) is never selected; its row then holds fewer than
+ *                min(topk, t+1) keys and is padded, still written in full.
  * out_topk_score [L, topk] fp32   scores aligned with out_idx, -inf padded; NULL to skip
  * out_dense_score [L, L] fp32     every score, -inf above the diagonal; NULL to skip;
  *                                 only for L <= 16384 (a debugging aid: the normal path

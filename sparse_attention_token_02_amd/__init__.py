@@ -153,11 +153,38 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def _workspace(nbytes: int, device, workspace):
+def _record(tensors, device, *streams):
+    """Tensors this binding allocated (on the current stream's pool) are used
+    by kernels enqueued on ``streams``: tell torch's caching allocator, so that
+    it does not hand their memory to other work before those kernels end."""
+    import torch
+    cur = torch.cuda.current_stream(device).cuda_stream
+    for s in streams:
+        if s is None:
+            continue
+        ts = torch.cuda.ExternalStream(s, device=device) if isinstance(s, int) else s
+        if ts.cuda_stream == cur:
+            continue
+        for t in tensors:
+            if t is not None:
+                t.record_stream(ts)
+
+
+def _workspace(nbytes: int, device, workspace, *streams):
     import torch
     if workspace is not None:
         return workspace
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    _record([ws], device, *streams)
+    return ws
+
+
+def _new(shape, dtype, device, stream):
+    """An output allocated here, recorded on the stream its kernels run on."""
+    import torch
+    t = torch.empty(shape, dtype=dtype, device=device)
+    _record([t], device, stream)
+    return t
 
 
 def dsa_indexer_topk_prefill_workspace(L: int, H: int, D: int, topk: int, dt) -> int:
@@ -176,12 +203,12 @@ def dsa_indexer_topk_prefill(q, q_scale, k, k_scale, w, topk: int, dt, *, q_scal
     L, H, D = q.shape
     dev = q.device
     if out_idx is None:
-        out_idx = torch.empty((L, topk), dtype=torch.int32, device=dev)
+        out_idx = _new((L, topk), torch.int32, dev, stream)
     if out_topk_score is None and want_scores:
-        out_topk_score = torch.empty((L, topk), dtype=torch.float32, device=dev)
+        out_topk_score = _new((L, topk), torch.float32, dev, stream)
     if out_dense_score is None and want_dense:
-        out_dense_score = torch.empty((L, L), dtype=torch.float32, device=dev)
-    ws = _workspace(dsa_indexer_topk_prefill_workspace(L, H, D, topk, dt), dev, workspace)
+        out_dense_score = _new((L, L), torch.float32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_prefill_workspace(L, H, D, topk, dt), dev, workspace, stream)
     _check(_lib.dsa_indexer_topk_prefill(
         _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), L, H, D, topk, _dt(dt),
         _ptr(out_idx), _ptr(out_topk_score), _ptr(out_dense_score), _ptr(ws), ws.numel(), _stream(stream)))
@@ -200,10 +227,10 @@ def dsa_indexer_topk_prefill_chunk(q, q_scale, k, k_scale, w, q_offset: int, top
     if k.shape[0] != q_offset + Lq:
         raise ValueError(f"k must hold q_offset + Lq = {q_offset + Lq} keys (has {k.shape[0]})")
     if out_idx is None:
-        out_idx = torch.empty((Lq, topk), dtype=torch.int32, device=dev)
+        out_idx = _new((Lq, topk), torch.int32, dev, stream)
     if out_topk_score is None and want_scores:
-        out_topk_score = torch.empty((Lq, topk), dtype=torch.float32, device=dev)
-    ws = _workspace(dsa_indexer_topk_prefill_workspace(Lq, H, D, topk, dt), dev, workspace)
+        out_topk_score = _new((Lq, topk), torch.float32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_prefill_workspace(Lq, H, D, topk, dt), dev, workspace, stream)
     _check(_lib.dsa_indexer_topk_prefill_chunk(
         _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), q_offset, Lq, H, D, topk,
         _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
@@ -230,10 +257,10 @@ def dsa_indexer_topk_prefill_varlen(q, q_scale, k, k_scale, w, cu_seqlens_q, cu_
     if cu_seqlens_k.numel() != nseq + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
     if out_idx is None:
-        out_idx = torch.empty((TQ, topk), dtype=torch.int32, device=dev)
+        out_idx = _new((TQ, topk), torch.int32, dev, stream)
     if out_topk_score is None and want_scores:
-        out_topk_score = torch.empty((TQ, topk), dtype=torch.float32, device=dev)
-    ws = _workspace(dsa_indexer_topk_prefill_varlen_workspace(nseq, TQ, H, D, topk, dt), dev, workspace)
+        out_topk_score = _new((TQ, topk), torch.float32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_prefill_varlen_workspace(nseq, TQ, H, D, topk, dt), dev, workspace, stream)
     _check(_lib.dsa_indexer_topk_prefill_varlen(
         _ptr(q), _ptr(q_scale), q_scale_head_stride, _ptr(k), _ptr(k_scale), _ptr(w), _ptr(cu_seqlens_q),
         _ptr(cu_seqlens_k), nseq, TQ, TK, H, D, topk, _dt(dt), _ptr(out_idx), _ptr(out_topk_score), _ptr(ws),
@@ -256,10 +283,10 @@ def dsa_indexer_topk_decode(q, w, k_cache, k_scale, seq_lens, topk: int, *, out_
     Lmax = k_cache.shape[1]
     dev = q.device
     if out_idx is None:
-        out_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+        out_idx = _new((B, topk), torch.int32, dev, stream)
     if out_topk_score is None and want_scores:
-        out_topk_score = torch.empty((B, topk), dtype=torch.float32, device=dev)
-    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace)
+        out_topk_score = _new((B, topk), torch.float32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace, stream)
     _check(_lib.dsa_indexer_topk_decode(
         _ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(seq_lens), B, Lmax, H, D, topk,
         _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
@@ -277,10 +304,10 @@ def dsa_indexer_topk_decode_paged(q, w, k_pages, k_scale_pages, block_table, seq
     max_blocks = block_table.shape[1]
     dev = q.device
     if out_idx is None:
-        out_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+        out_idx = _new((B, topk), torch.int32, dev, stream)
     if out_topk_score is None and want_scores:
-        out_topk_score = torch.empty((B, topk), dtype=torch.float32, device=dev)
-    ws = _workspace(dsa_indexer_topk_decode_workspace(B, max_blocks * page, H, D, topk), dev, workspace)
+        out_topk_score = _new((B, topk), torch.float32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, max_blocks * page, H, D, topk), dev, workspace, stream)
     _check(_lib.dsa_indexer_topk_decode_paged(
         _ptr(q), _ptr(w), _ptr(k_pages), _ptr(k_scale_pages), num_pages, page, _ptr(block_table), max_blocks,
         _ptr(seq_lens), B, H, D, topk, _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
@@ -313,8 +340,8 @@ def indexcache_run_layers(pattern: str, q, q_scale, k, k_scale, w, topk: int, dt
     L, H, D = q[f0].shape
     dev = q[f0].device
     if tcache is None:
-        tcache = torch.empty((L, topk), dtype=torch.int32, device=dev)
-    ws = _workspace(dsa_indexer_topk_prefill_workspace(L, H, D, topk, dt), dev, workspace)
+        tcache = _new((L, topk), torch.int32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_prefill_workspace(L, H, D, topk, dt), dev, workspace, stream)
     src = (ctypes.c_int32 * max(N, 1))()
     errors = []
 
@@ -349,8 +376,8 @@ def indexcache_run_decode_layers(pattern: str, q, w, k_cache, k_scale, seq_lens,
     Lmax = k_cache[f0].shape[1]
     dev = q[f0].device
     if tcache is None:
-        tcache = torch.empty((B, topk), dtype=torch.int32, device=dev)
-    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace)
+        tcache = _new((B, topk), torch.int32, dev, stream)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace, stream)
     src = (ctypes.c_int32 * max(N, 1))()
     errors = []
 
@@ -431,11 +458,16 @@ def indexcache_run_decode_layers_mli(pattern: str, q, w, k_cache, k_scale, seq_l
     nf = pattern.count("F")
     if sel_buf is None:
         sel_buf = torch.empty((max(nf, 1), B, topk), dtype=torch.int32, device=dev)
+        sel_alloc = True
+    else:
+        sel_alloc = False
     if sel_buf.shape[0] < nf or tuple(sel_buf.shape[1:]) != (B, topk) or not sel_buf.is_contiguous():
         raise ValueError(f"sel_buf must be a contiguous [{nf}+, {B}, {topk}] int32 tensor")
-    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace)
     if side_stream is None:
         side_stream = torch.cuda.Stream(device=dev)
+    ws = _workspace(dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dev, workspace, stream, side_stream)
+    if sel_alloc:   # written on the side stream, read on `stream`
+        _record([sel_buf], dev, stream, side_stream)
     src = (ctypes.c_int32 * max(N, 1))()
     slots = {sel_buf[i].data_ptr(): sel_buf[i] for i in range(sel_buf.shape[0])}
     errors = []
@@ -470,8 +502,8 @@ def standin_sparse_attention(q, latent, sel, scale: float, *, out=None, workspac
     Lmax = latent.shape[1]
     topk = sel.shape[1]
     if out is None:
-        out = torch.empty((B, 512), dtype=torch.float32, device=q.device)
-    ws = _workspace(standin_sparse_attention_workspace(B, topk), q.device, workspace)
+        out = _new((B, 512), torch.float32, q.device, stream)
+    ws = _workspace(standin_sparse_attention_workspace(B, topk), q.device, workspace, stream)
     _check(_lib.standin_sparse_attention(_ptr(q), _ptr(latent), _ptr(sel), B, Lmax, topk, float(scale), _ptr(out),
                                          _ptr(ws), ws.numel(), _stream(stream)))
     return out
@@ -488,7 +520,7 @@ def topk_overlap_matrix(idx, topk: int, *, row_begin=None, row_end=None, row_str
     rb = topk - 1 if row_begin is None else row_begin
     re_ = L if row_end is None else row_end
     if out_counts is None:
-        out_counts = torch.empty((N, N), dtype=torch.uint64, device=idx[0].device)
+        out_counts = _new((N, N), torch.uint64, idx[0].device, stream)
     r = np.empty((N, N), dtype=np.float64) if ratio else None
     rp = r.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if ratio else None
     _check(_lib.topk_overlap_matrix(_ptr_array(idx), N, L, topk, rb, re_, row_stride, _ptr(out_counts), rp,

@@ -19,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdsa_indexer.so")
 SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "overlap.hip", "attention.hip"]
+# measured device peaks (matrix-core and HBM microbenchmarks), for the benchmark
+PEAK_OUT = os.path.join(PKG, "libdsa_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -42,18 +45,27 @@ def _compile(src: str, obj_dir: str, extra: list[str]) -> str:
     return obj
 
 
-def build(jobs: int = 8, extra: list[str] | None = None, out: str = OUT) -> str:
-    extra = list(extra or [])
-    obj_dir = os.path.join(ROOT, "_build", "dsa_indexer")
-    os.makedirs(obj_dir, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, obj_dir, extra), SOURCES))
+def _link(objs: list[str], out: str) -> str:
     tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     shutil.move(tmp, out)
+    return out
+
+
+def build(jobs: int = 8, extra: list[str] | None = None, out: str = OUT, peak: bool = True) -> str:
+    """Builds libdsa_indexer.so (to `out`) and, unless peak is False, libdsa_peak.so."""
+    extra = list(extra or [])
+    obj_dir = os.path.join(ROOT, "_build", "dsa_indexer")
+    os.makedirs(obj_dir, exist_ok=True)
+    srcs = SOURCES + (PEAK_SOURCES if peak else [])
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, obj_dir, extra), srcs)))
+    _link([objs[s] for s in SOURCES], out)
+    if peak:
+        _link([objs[s] for s in PEAK_SOURCES], PEAK_OUT)
     return out
 
 

@@ -40,10 +40,7 @@ namespace {
 constexpr int DS_NT = 256;          // score kernel threads
 constexpr int DS_NSUB = 64;         // 32-key steps per wave
 static_assert(DS_NSUB <= 64, "paged lookup: one lane per step");
-#ifndef DS_PF_STEPS
-#define DS_PF_STEPS 4
-#endif
-constexpr int DS_PF = DS_PF_STEPS;  // steps in flight per wave
+constexpr int DS_PF = 4;            // steps in flight per wave
 constexpr int DS_KPB = (DS_NT / 64) * DS_NSUB * 32;   // keys per workgroup
 constexpr int DS_MAXWG = 32;        // score workgroups per sequence at most (Lmax <= 262144)
 constexpr int HBINS = 4096;         // fine bins: top 12 bits of the order-preserving key

@@ -599,9 +599,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int t = t0 + rl;
         if (t < L && sh.row_cnt[rl] < min(p.topk, t + 1)) short_row = true;
       }
-      if (short_row) {          // uniform: every thread read the same counts
+      // Only a sample threshold can make a row short with finite scores: the
+      // item is then recomputed without it.  Without a sample (always so on
+      // the second attempt) a short row has keys whose score is NaN or -inf,
+      // which never pass the filter; the final selection writes what the
+      // row holds and pads the rest.
+      if (short_row && stile > 0) {   // uniform: every thread read the same counts
         __syncthreads();
-        continue;               // recompute the item without the sample threshold
+        continue;
       }
 
       // ---- final selection: each wave writes its own rows, in ascending key

@@ -26,3 +26,43 @@ def pytest_configure(config):
     if not os.path.exists(syn):
         import synth.gpu as sg
         sg.build()
+
+
+# ---- parity report: rows compared, rows the rounding floor decided, and the
+# worst score errors, per test (printed in the terminal summary)
+_PARITY_REPORT = []
+
+
+def pytest_runtest_call(item):
+    try:
+        from tests import parity
+    except Exception:
+        return
+    parity.reset_stats()
+
+
+def pytest_runtest_teardown(item, nextitem):
+    try:
+        from tests import parity
+    except Exception:
+        return
+    st = dict(parity.STATS)
+    if st["rows"]:
+        _PARITY_REPORT.append((item.nodeid, st, parity.take_floor_rows()))
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    if not _PARITY_REPORT:
+        return
+    tr = terminalreporter
+    tr.section("parity: rows checked / floor-decided rows / worst score error")
+    tot_rows = tot_floor = 0
+    for nodeid, st, floor in _PARITY_REPORT:
+        tot_rows += st["rows"]
+        tot_floor += st["floor_rows"]
+        line = (f"{nodeid}: rows {st['rows']}, floor-decided {st['floor_rows']}, "
+                f"max |err|/|o| {st['max_err_rel_o']:.2e} (|o| >= 0.1 A), max |err|/A {st['max_err_rel_A']:.2e}")
+        if floor:
+            line += " | floor rows (id, max |o-tau|/|tau|): " + ", ".join(f"({r}, {d:.2e})" for r, d in floor[:8])
+        tr.write_line(line)
+    tr.write_line(f"total: {tot_rows} rows, {tot_floor} floor-decided")

@@ -327,3 +327,16 @@ def test_one_hip_runtime_in_process():
     maps = open("/proc/self/maps").read().splitlines()
     paths = {l.split()[-1] for l in maps if "libamdhip64" in l}
     assert len(paths) == 1, paths
+
+
+def test_peak_library_exports_its_header():
+    """The measured-peak library used by the benchmark exports every function
+    include/dsa_peak.h declares (no kernel is launched here)."""
+    from sparse_attention_token_02_amd import peak
+    text = open(os.path.join(ROOT, "include", "dsa_peak.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^int\s+(\w+)\s*\(", text, flags=re.M)
+    lib = ctypes.CDLL(peak.LIB_PATH)
+    assert set(names) == set(peak.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n

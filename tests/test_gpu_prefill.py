@@ -56,11 +56,14 @@ def test_tiny_bf16_every_row_and_dense_scores(dsa):
     rows = np.arange(cfg["L"])
     res = _oracle_rows(inp, cfg, rows)
     _compare(idx, sc, res, rows, cfg["topk"])
-    worst = 0.0
+    worst_a = worst_o = 0.0
     for t in rows:
         assert parity.check_dense(dense[t], res["o"][t], res["A"][t]) is None, t
-        worst = max(worst, parity.max_rel_err(dense[t][: t + 1], res["o"][t], res["A"][t])[0])
-    assert worst < 2e-3
+        ea, eo = parity.max_rel_err(dense[t][: t + 1], res["o"][t], res["A"][t])
+        worst_a, worst_o = max(worst_a, ea), max(worst_o, eo)
+    print(f"tiny dense scores: max |err|/A {worst_a:.3g}, max |err|/|o| (|o| >= 0.1 A) {worst_o:.3g}")
+    assert worst_o <= parity.SCORE_RTOL
+    assert worst_a <= parity.SCORE_RTOL * parity.SCORE_FLOOR_A
 
 
 @pytest.mark.parametrize("L,topk", [(1000, 100), (777, 64)])
@@ -217,3 +220,33 @@ def test_topk_limits(dsa, L, topk):
     check_structure_all(idx, topk)
     rows = sample_rows(L, topk, 24, seed=topk)
     _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
+
+
+def test_overflowing_scores_still_write_every_row(dsa):
+    """Finite but extreme head weights on some rows overflow their scores to
+    inf and NaN (mixed signs).  A NaN or -inf score is never selected, so
+    such a row may hold fewer than min(k, t+1) keys, but every row is still
+    written in full (the sentinel the output starts with is gone, -1 padded),
+    and the rows with ordinary weights still match the oracle."""
+    import torch
+    L, topk = 3000, 64
+    cfg = dict(gen.CONFIGS["prefill_32k"], L=L, topk=topk, heavy_count=30)
+    note(f"prefill overflowing weights L={L} k={topk}")
+    inp = gen.prefill_inputs(cfg)
+    w = inp["w"].copy()
+    hot = np.arange(1000, 1100)
+    big = gen.bf16_bits(np.float32(3.0e38))
+    w[hot, 0::2] = big
+    w[hot, 1::2] = big | np.uint16(0x8000)       # the same magnitude, negative
+    inp = dict(inp, w=w)
+    out = torch.full((L, topk), 0x7FFFFFFF, dtype=torch.int32, device="cuda")
+    idx, sc, _ = _run(dsa, inp, cfg, want_scores=True, out_idx=out)
+    idx = host(idx)
+    assert not np.any(idx == 0x7FFFFFFF), "a row was left unwritten"
+    for t in hot:
+        v = idx[t][idx[t] >= 0]
+        m = len(v)
+        assert m <= min(topk, t + 1)
+        assert np.all(idx[t][m:] == -1) and np.all(v <= t) and np.all(np.diff(v) > 0), t
+    rows = np.array(sorted(set(sample_rows(L, topk, 24).tolist()) - set(hot.tolist())), dtype=np.int64)
+    _compare(idx, host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
