@@ -60,7 +60,7 @@ def test_paged_equals_contiguous_and_oracle(dsa, page, H, D):
     res = oracle.decode(q, w, cache, ks, lens, topk, return_scores=True)
     ih, sh = host(idx_p), host(sc_p)
     for b in range(B):
-        assert parity.check_row(ih[b], res["o"][b], res["A"][b], topk, g_score=sh[b]) is None, b
+        assert parity.check_row(ih[b], res["o"][b], res["A"][b], topk, g_score=sh[b], fmt="bf16") is None, b
 
 
 def test_paged_128k_batch_equals_contiguous(dsa):

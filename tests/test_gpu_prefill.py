@@ -37,11 +37,11 @@ def _oracle_rows(inp, cfg, rows):
                           cfg["topk"], rows=rows, return_scores=True)
 
 
-def _compare(idx, sc, res, rows, topk):
+def _compare(idx, sc, res, rows, topk, fmt="fp8"):
     bad = []
     for r, t in enumerate(rows):
         err = parity.check_row(idx[t], res["o"][r], res["A"][r], topk,
-                               g_score=None if sc is None else sc[t])
+                               g_score=None if sc is None else sc[t], fmt=fmt)
         if err:
             bad.append((int(t), err))
     assert not bad, f"{len(bad)} rows differ, first: {bad[:3]}"
@@ -55,7 +55,7 @@ def test_tiny_bf16_every_row_and_dense_scores(dsa):
     idx, sc, dense = host(idx), host(sc), host(dense)
     rows = np.arange(cfg["L"])
     res = _oracle_rows(inp, cfg, rows)
-    _compare(idx, sc, res, rows, cfg["topk"])
+    _compare(idx, sc, res, rows, cfg["topk"], fmt="bf16")
     worst_a = worst_o = 0.0
     for t in rows:
         assert parity.check_dense(dense[t], res["o"][t], res["A"][t]) is None, t
@@ -189,7 +189,7 @@ def test_every_built_configuration(dsa, dt, H, D):
     idx, sc, _ = _run(dsa, inp, cfg, want_scores=True)
     check_structure_all(idx, topk)
     rows = sample_rows(L, topk, 48, seed=H * D)
-    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
+    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk, fmt=dt)
 
 
 @pytest.mark.parametrize("dt,H,D", BUILT)
@@ -207,7 +207,7 @@ def test_every_built_configuration_with_key_sample(dsa, dt, H, D):
     check_structure_all(idx, topk)
     around = {2047, 2048, 2049, 2055, 2056, 4095, 4096, 4097, 4103, 4104}
     rows = np.array(sorted(set(sample_rows(L, topk, 20, seed=H + D).tolist()) | around), dtype=np.int64)
-    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
+    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk, fmt=dt)
 
 
 @pytest.mark.parametrize("L,topk", [(700, 1), (5003, 4096)])

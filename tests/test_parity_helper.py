@@ -46,14 +46,14 @@ def test_swap_inside_strict_band_passes_without_floor():
     alt, o2 = _swapped(o, 128, 5e-4)
     parity.reset_stats()
     # A small enough that the rounding floor is far below the band
-    assert parity.check_row(alt, o2, np.full_like(A, 1e-6), 128) is None
+    assert parity.check_row(alt, o2, np.full_like(A, 1e-6), 128, fmt="bf16") is None
     assert parity.STATS["floor_rows"] == 0
 
 
 def test_swap_just_outside_strict_band_fails_when_rounding_cannot_explain_it():
     idx, sc, o, A = _row()
     alt, o2 = _swapped(o, 128, 2e-3)
-    assert parity.check_row(alt, o2, np.full_like(A, 1e-6), 128) is not None
+    assert parity.check_row(alt, o2, np.full_like(A, 1e-6), 128, fmt="bf16") is not None
 
 
 def test_swap_explained_by_rounding_is_floor_decided_and_counted():
@@ -62,17 +62,18 @@ def test_swap_explained_by_rounding_is_floor_decided_and_counted():
     tau = abs(o[kth])
     alt, o2 = _swapped(o, 128, 2e-3)
     # a magnitude whose rounding bound covers a 2e-3 relative gap on each side
-    bigA = np.full_like(A, 2e-3 * tau / parity.fp32_error_bound(1.0))
+    bigA = np.full_like(A, 2e-3 * tau / parity.fp32_error_bound(1.0, fmt="bf16"))
     parity.reset_stats()
-    assert parity.check_row(alt, o2, bigA, 128, row_id=7) is None
+    assert parity.check_row(alt, o2, bigA, 128, row_id=7, fmt="bf16") is None
     assert parity.STATS["floor_rows"] == 1
     assert parity.take_floor_rows()[0][0] == 7
 
 
 def test_error_bound_value():
-    # (D + H + 4) u with the 1% margin, at H=64, D=128
-    assert np.isclose(parity.fp32_error_bound(1.0), 1.01 * 196 * 2.0 ** -24)
-    assert np.isclose(parity.fp32_error_bound(1.0, terms=72), 1.01 * 76 * 2.0 ** -24)
+    # bf16: (D + H + 4) u with the 1% margin; fp8 adds the matrix-core group loss 7 * 2^-13
+    assert np.isclose(parity.fp32_error_bound(1.0, fmt="bf16"), 1.01 * 196 * 2.0 ** -24)
+    assert np.isclose(parity.fp32_error_bound(1.0, terms=72, fmt="bf16"), 1.01 * 76 * 2.0 ** -24)
+    assert np.isclose(parity.fp32_error_bound(1.0), 7 * 2.0 ** -13 + 1.01 * 196 * 2.0 ** -24)
 
 
 def test_structure_errors():
