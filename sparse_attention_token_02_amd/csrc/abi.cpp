@@ -149,33 +149,23 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   return DSA_OK;
 }
 
-// Decode workspace: score rows [B, ld] fp32, per-workgroup histograms,
-// selection bitmaps, candidate keys and indices [B, Lmax] each, candidate
-// counts and the per-sequence cut (bin of the k-th score, keys above it).
+// Decode workspace: per score workgroup of each sequence, its packed
+// histograms, its list's cut (lowest bin kept, entries) and its list of
+// (key, index) candidates.
 struct DecodeWs {
-  size_t scores, hist, bitmap, ckey, cidx, ccnt, cut, total;
-  int ld;
+  size_t hist, wgcut, cand, total;
 };
 
 DecodeWs decode_ws(int B, int Lmax) {
   DecodeWs w{};
-  w.ld = (int)align_up((size_t)Lmax, 64);
-  size_t off = 0;
-  w.scores = off;
-  off += align_up((size_t)B * w.ld * 4, 256);
-  w.hist = off;
   const dsa::DecodeWsSizes z = dsa::decode_ws_sizes(Lmax);
+  size_t off = 0;
+  w.hist = off;
   off += align_up((size_t)B * z.hist_words * 4, 256);
-  w.bitmap = off;
-  off += align_up((size_t)B * z.bitmap_words * 4, 256);
-  w.ckey = off;
-  off += align_up((size_t)B * Lmax * 4, 256);
-  w.cidx = off;
-  off += align_up((size_t)B * Lmax * 4, 256);
-  w.ccnt = off;
-  off += align_up((size_t)B * z.cand_cnt * 4, 256);
-  w.cut = off;
-  off += align_up((size_t)B * 8, 256);
+  w.wgcut = off;
+  off += align_up((size_t)B * z.nwg * 8, 256);
+  w.cand = off;
+  off += align_up((size_t)B * z.cand_entries * 8, 256);
   w.total = off;
   return w;
 }
@@ -229,14 +219,9 @@ dsa_status launch_decode(const DecodeArgs& a) {
   p.out_score = a.out_score;
   uint8_t* base = static_cast<uint8_t*>(a.ws);
   const DecodeWs lay = decode_ws(a.B, a.Lmax);
-  p.ld = lay.ld;
-  p.scores = reinterpret_cast<float*>(base + lay.scores);
   p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
-  p.cand_key = reinterpret_cast<uint32_t*>(base + lay.ckey);
-  p.cand_idx = reinterpret_cast<int*>(base + lay.cidx);
-  p.bitmap = reinterpret_cast<uint32_t*>(base + lay.bitmap);
-  p.cand_cnt = reinterpret_cast<int*>(base + lay.ccnt);
-  p.cut = reinterpret_cast<int2*>(base + lay.cut);
+  p.wgcut = reinterpret_cast<int2*>(base + lay.wgcut);
+  p.cand = reinterpret_cast<uint2*>(base + lay.cand);
   p.block_table = a.block_table;
   p.max_blocks = a.max_blocks;
   p.page_shift = a.page_size > 0 ? __builtin_ctz((unsigned)a.page_size) : 0;

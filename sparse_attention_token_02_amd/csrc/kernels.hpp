@@ -57,14 +57,9 @@ struct DecodeParams {
   int topk;
   int32_t* out_idx;          // [B, topk]
   float* out_score;          // [B, topk], nullable
-  int ld;                    // row stride of the score rows (Lmax rounded up to 64)
-  float* scores;             // workspace [B, ld]
-  uint32_t* hist;            // workspace [B, hist_words]: per-workgroup 16-bit histograms
-  uint32_t* bitmap;          // workspace [B, bitmap_words]: selected keys
-  uint32_t* cand_key;        // workspace [B, Lmax]
-  int* cand_idx;             // workspace [B, Lmax]
-  int* cand_cnt;             // workspace [B, cand_cnt]: candidates per select workgroup
-  int2* cut;                 // workspace [B]: bin of the k-th score, keys in higher bins
+  uint32_t* hist;            // workspace [B, nwg, PW]: per-workgroup 16-bit histograms
+  int2* wgcut;               // workspace [B, nwg]: per list (lowest bin kept, entries)
+  uint2* cand;               // workspace [B, nwg, keys per workgroup]: (key, index) lists
   // paged cache (block_table != null): cache = pages [num_pages, 2^page_shift, D],
   // k_scale = [num_pages, 2^page_shift]; token s of sequence b lives in page
   // block_table[b * max_blocks + (s >> page_shift)]; Lmax = max_blocks << page_shift
@@ -74,8 +69,9 @@ struct DecodeParams {
   int num_pages;
 };
 
+// per sequence: score workgroups, histogram words, list entries
 struct DecodeWsSizes {
-  size_t hist_words, bitmap_words, cand_cnt;
+  size_t nwg, hist_words, cand_entries;
 };
 
 // Stand-in sparse attention (one head): latent rows of STANDIN_DK bf16 values,

@@ -16,7 +16,7 @@ Contract
   swapped key lies within E(s) + max E over the swapped keys of tau.  Such
   rows are "floor-decided"; they are counted in STATS and reported per test.
 * Rounding bound of a device score, by input format:
-  - bf16 (and the decode path, whose fp8 keys are widened exactly to bf16):
+  - bf16 (bf16 inputs on the bf16 matrix cores):
     the dot product's D exact products take at most D - 1 fp32 roundings
     (gamma_D), the weighted head sum at most H (gamma_H), and the folded
     weight w * q_scale, the ReLU product and k_scale one each:
@@ -29,6 +29,16 @@ Contract
     to 1.1e-4 of the sum of |products|).  Each of the other 7 products of a
     group can lose < 2^-13 of the group's largest, so
     E(s) = (7 * 2^-13 + 1.01 (D + H + 4) 2^-24) A(s).
+  - fp8q (the decode path: fp8 keys against a bf16 query split into
+    two e4m3 limbs with e8m0 scales per block of 32 dimensions, both limbs
+    on the fp8 matrix cores).  The split loses at most 2^-22 of the block's
+    largest |q| per element (it is exact when a block spans at most 2^14 in
+    magnitude), and the limbs' magnitudes add up to at most 1.125 |q_i| +
+    2^-16 max|q| per element, which scales the fp8 term above.  With
+    M(s) = k_scale(s) sum_h |w_h| max_i |q_h,i| sum_i |k_s,i|:
+    E(s) = 1.125 (7 * 2^-13 + 1.01 (D + H + 4) 2^-24) A(s) + 2^-21 M(s).
+    tests/test_parity_helper.py checks both limits on an emulation of the
+    split.
   `terms` = D + H (192 at H=64, D=128, the largest built shape).  The bound
   is a worst case: the measured worst errors are about 1e-6 A (fp8) and
   1e-8 A (bf16), and the per-test report shows how many rows needed the
@@ -67,12 +77,36 @@ def take_floor_rows() -> list:
 
 
 FP8_GROUP_LOSS = 7 * 2.0 ** -13   # fp8 matrix-core groups of 8 products (see module doc)
+QLIMB_MAG = 1.125                 # limb magnitudes against |q| (fp8q)
+QLIMB_LOSS = 2.0 ** -21           # split loss and limb magnitude slack against M (fp8q)
 
 
-def fp32_error_bound(A, terms: int = DEFAULT_TERMS, fmt: str = "fp8"):
-    """Bound on |device score - exact score| for magnitude A (see module doc)."""
+def fp32_error_bound(A, terms: int = DEFAULT_TERMS, fmt: str = "fp8", M=None):
+    """Bound on |device score - exact score| for magnitude A (and, for fmt
+    "fp8q", the query-block magnitude M; see module doc)."""
+    A = np.asarray(A, dtype=np.float64)
+    if fmt == "fp8q":
+        if M is None:
+            raise ValueError("fmt='fp8q' needs M")
+        rel = QLIMB_MAG * (1.01 * (terms + 4) * U32 + FP8_GROUP_LOSS)
+        return rel * A + QLIMB_LOSS * np.asarray(M, dtype=np.float64)
+    if fmt not in ("fp8", "bf16"):
+        raise ValueError(f"unknown format {fmt!r}")
     rel = 1.01 * (terms + 4) * U32 + (FP8_GROUP_LOSS if fmt == "fp8" else 0.0)
-    return rel * np.asarray(A, dtype=np.float64)
+    return rel * A
+
+
+def decode_query_mag(q, w, cache, k_scale, lens) -> list:
+    """M for every sequence of a decode batch: per sequence b, the array over
+    s < lens[b] of k_scale[b, s] * sum_h |w[b, h]| max_i |q[b, h, i]| *
+    sum_i |k[b, s, i]| (dequantised inputs)."""
+    import oracle
+    out = []
+    for b in range(len(lens)):
+        n = int(lens[b])
+        g = float(np.sum(np.abs(oracle.dec_bf16(w[b])) * np.max(np.abs(oracle.dec_bf16(q[b])), axis=1)))
+        out.append(g * np.sum(np.abs(oracle.dequant(cache[b, :n], k_scale[b, :n], "fp8")), axis=1))
+    return out
 
 
 def score_limit(o, A):
@@ -109,7 +143,7 @@ def check_structure(g_idx: np.ndarray, n: int, k: int) -> str | None:
 
 
 def check_row(g_idx, o, A, k, g_score=None, terms: int = DEFAULT_TERMS, row_id=None,
-              fmt: str = "fp8") -> str | None:
+              fmt: str = "fp8", M=None) -> str | None:
     """Returns None when the device row matches the oracle row, else a reason."""
     o = np.asarray(o, dtype=np.float64)
     A = np.asarray(A, dtype=np.float64)
@@ -132,7 +166,7 @@ def check_row(g_idx, o, A, k, g_score=None, terms: int = DEFAULT_TERMS, row_id=N
         if diff.size:
             dist = np.abs(o[diff] - tau)
             strict = dist <= BAND_REL * abs(tau)
-            E = fp32_error_bound(A[diff], terms, fmt)
+            E = fp32_error_bound(A[diff], terms, fmt, None if M is None else np.asarray(M)[diff])
             floor = E + E.max()
             ok = strict | (dist <= floor)
             if not np.all(ok):

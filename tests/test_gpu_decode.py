@@ -39,8 +39,9 @@ def _run(dsa, inp, topk):
 def _compare(idx, sc, inp, topk, seqs=None):
     seqs = range(len(inp["lens"])) if seqs is None else seqs
     res = oracle.decode(inp["q"], inp["w"], inp["cache"], inp["k_scale"], inp["lens"], topk, return_scores=True)
+    M = parity.decode_query_mag(inp["q"], inp["w"], inp["cache"], inp["k_scale"], inp["lens"])
     for b in seqs:
-        err = parity.check_row(idx[b], res["o"][b], res["A"][b], topk, g_score=sc[b], fmt="bf16")
+        err = parity.check_row(idx[b], res["o"][b], res["A"][b], topk, g_score=sc[b], fmt="fp8q", M=M[b])
         assert err is None, (b, err)
 
 
@@ -101,8 +102,9 @@ def test_decode_128k_full_size_sampled_sequences(dsa, ragged):
     assert np.array_equal(host(d["cache"][seqs[1]]), hi["cache"][1])
     assert np.array_equal(host(d["k_scale"][seqs[2]]), hi["k_scale"][2])
     res = oracle.decode(hi["q"], hi["w"], hi["cache"], hi["k_scale"], hi["lens"], cfg["topk"], return_scores=True)
+    M = parity.decode_query_mag(hi["q"], hi["w"], hi["cache"], hi["k_scale"], hi["lens"])
     for i, b in enumerate(seqs):
-        err = parity.check_row(idx[b], res["o"][i], res["A"][i], cfg["topk"], g_score=sc[b], fmt="bf16")
+        err = parity.check_row(idx[b], res["o"][i], res["A"][i], cfg["topk"], g_score=sc[b], fmt="fp8q", M=M[i])
         assert err is None, (b, err)
     lens = gen.decode_lens(cfg)
     for b in range(cfg["B"]):

@@ -58,9 +58,11 @@ def test_paged_equals_contiguous_and_oracle(dsa, page, H, D):
     torch.cuda.synchronize()
     assert torch.equal(idx_p, idx_c) and torch.equal(sc_p, sc_c)
     res = oracle.decode(q, w, cache, ks, lens, topk, return_scores=True)
+    M = parity.decode_query_mag(q, w, cache, ks, lens)
     ih, sh = host(idx_p), host(sc_p)
     for b in range(B):
-        assert parity.check_row(ih[b], res["o"][b], res["A"][b], topk, g_score=sh[b], fmt="bf16") is None, b
+        assert parity.check_row(ih[b], res["o"][b], res["A"][b], topk, g_score=sh[b], fmt="fp8q",
+                                M=M[b]) is None, b
 
 
 def test_paged_128k_batch_equals_contiguous(dsa):

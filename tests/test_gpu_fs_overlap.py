@@ -163,10 +163,13 @@ def test_fs_decode_driver_matches_oracle(dsa):
     want, osrc, calls = oracle.fs_run(pattern, lambda l: oracle.decode(
         hl[l]["q"], hl[l]["w"], hl[l]["cache"], hl[l]["k_scale"], hl[l]["lens"], topk, return_scores=True))
     assert osrc == src and calls == pattern.count("F")
+    M = {l: parity.decode_query_mag(hl[l]["q"], hl[l]["w"], hl[l]["cache"], hl[l]["k_scale"], hl[l]["lens"])
+         for l in range(N) if hl[l]}
     for l in range(N):
         got = host(seen[l][3])
         for b in range(B):
-            assert parity.check_row(got[b], want[l]["o"][b], want[l]["A"][b], topk, fmt="bf16") is None, (l, b)
+            assert parity.check_row(got[b], want[l]["o"][b], want[l]["A"][b], topk, fmt="fp8q",
+                                    M=M[src[l]][b]) is None, (l, b)
         if pattern[l] == "S":
             assert torch.equal(seen[l][3], seen[src[l]][3]), l
         else:

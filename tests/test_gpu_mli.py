@@ -99,8 +99,10 @@ def test_mli_schedule_matches_oracle_and_waits_for_each_selection(dsa):
         s = asrc[l]
         assert torch.equal(got_sel[l], alone[s]), (l, s)
         g = host(got_sel[l])
+        M = parity.decode_query_mag(hl[s]["q"], hl[s]["w"], hl[s]["cache"], hl[s]["k_scale"], hl[s]["lens"])
         for b in range(B):
-            assert parity.check_row(g[b], want[l]["o"][b], want[l]["A"][b], topk, fmt="bf16") is None, (l, b)
+            assert parity.check_row(g[b], want[l]["o"][b], want[l]["A"][b], topk, fmt="fp8q",
+                                    M=M[b]) is None, (l, b)
         ref = oracle.standin_attention(host(qa[l]), host(lat[l % 2]), g, 0.5)
         np.testing.assert_allclose(host(got_out[l]).astype(np.float64), ref, rtol=1e-4, atol=2e-6)
     # lagged: the F layers 2, 3, 5, 6 attend the previous F layer, not themselves

@@ -1,5 +1,6 @@
 """The parity contract itself, exercised with mistakes planted in oracle outputs."""
 import numpy as np
+import pytest
 
 import oracle
 from synth import gen
@@ -123,3 +124,52 @@ def test_dense_check_uses_the_same_score_rule():
     bad = row.copy()
     bad[n] = 0.0                                   # a masked key must stay -inf
     assert parity.check_dense(bad, o, A) is not None
+
+
+def _e4m3_round(v):
+    """Nearest OCP e4m3 value of v (|v| <= 448), ties to even, in float64:
+    a grid of 2^-9 below 2^-6, else 3 mantissa bits at v's exponent."""
+    a = np.abs(v)
+    ulp = np.where(a < 2.0 ** -6, 2.0 ** -9, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+    return np.sign(v) * np.round(a / ulp) * ulp
+
+
+def _limb(v):
+    """One limb of a block (rows of v): e4m3 values on the grid 2^e set by the
+    block maximum m (m 2^-e in (224, 448]); blocks with m < 2^-100 give 0."""
+    m = np.max(np.abs(v), axis=1, keepdims=True)
+    E = np.floor(np.log2(np.maximum(m, 2.0 ** -100)))
+    e = np.where(m / np.exp2(E) <= 1.75, E - 8, E - 7)
+    out = _e4m3_round(v * np.exp2(-e)) * np.exp2(e)
+    return np.where(m >= 2.0 ** -100, out, 0.0)
+
+
+def test_fp8q_query_split_limits():
+    """The two-limb split of a bf16 query block that the fp8q bound assumes:
+    loss <= 2^-22 of the block maximum, none when the block spans <= 2^14,
+    and limb magnitudes <= 1.125 |q| + 2^-16 max |q|."""
+    rng = np.random.default_rng(3)
+    n = 6000
+    spread = np.concatenate([np.zeros(n // 3), rng.uniform(1, 14, n // 3), rng.uniform(14, 40, n - 2 * (n // 3))])
+    x = rng.standard_normal((n, 32)) * np.exp2(rng.uniform(0, 1, (n, 32)) * spread[:, None] - spread[:, None] / 2)
+    x *= np.exp2(rng.integers(-60, 60, (n, 1)).astype(np.float64))
+    u = x.astype(np.float32).view(np.uint32)
+    q = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32).view(np.float32).astype(np.float64)
+    l0 = _limb(q)
+    l1 = _limb(q - l0)
+    m = np.max(np.abs(q), axis=1, keepdims=True)
+    err = np.abs(l0 + l1 - q)
+    assert np.all(err <= 2.0 ** -22 * m)
+    nz = np.where(q != 0, np.abs(q), np.inf)
+    narrow = (m[:, 0] <= 2.0 ** 14 * np.min(nz, axis=1))
+    assert narrow.sum() > n // 3 and np.all(err[narrow] == 0)
+    assert np.all(np.abs(l0) + np.abs(l1) <= 1.125 * np.abs(q) + 2.0 ** -16 * m)
+    assert np.max(err / m) > 2.0 ** -30          # the wide blocks do lose bits
+
+
+def test_fp8q_bound_terms():
+    assert np.isclose(parity.fp32_error_bound(1.0, fmt="fp8q", M=0.0),
+                      1.125 * (7 * 2.0 ** -13 + 1.01 * 196 * 2.0 ** -24))
+    assert np.isclose(parity.fp32_error_bound(0.0, fmt="fp8q", M=1.0), 2.0 ** -21)
+    with pytest.raises(ValueError):
+        parity.fp32_error_bound(1.0, fmt="fp8q")
