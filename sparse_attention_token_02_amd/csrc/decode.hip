@@ -101,10 +101,11 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   __shared__ uint32_t hist[HBINS];
   // per-wave transpose of one 32-key step: row r (a key), chunk c stored at
   // chunk position c ^ swz(r), swz(r) = (r / RPB) % CPR, so both the
-  // row-contiguous writes and the per-key operand reads are conflict-free
+  // row-contiguous writes and the per-key operand reads are conflict-free;
+  // at the start, the query's limbs in operand order
   __shared__ __attribute__((aligned(16))) uint8_t ktr[DS_WAVES][32 * D];
   // order-preserving keys of the workgroup's scores; at the start, the
-  // query's limbs in operand order
+  // limbs' scales
   __shared__ __attribute__((aligned(16))) float sc_stage[DS_KPB];
   __shared__ int sh_cut[2];
 
@@ -181,9 +182,9 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // limb 4).  Staged in operand order, [mb][kk][c][lane][16 bytes] with
   // kk = limb * KS + ks, and one scale word per (mb, lane): byte kk for lane
   // (row, c).
-  uint8_t* lstage = reinterpret_cast<uint8_t*>(sc_stage);
-  int* lscale = reinterpret_cast<int*>(lstage + MB * NK * 2 * 64 * 16);
-  static_assert(MB * NK * 2 * 64 * 16 + MB * 64 * 4 <= (int)sizeof(sc_stage), "limb staging");
+  uint8_t* lstage = &ktr[0][0];
+  int* lscale = reinterpret_cast<int*>(sc_stage);
+  static_assert(MB * NK * 2 * 64 * 16 <= (int)sizeof(ktr) && MB * 64 * 4 <= (int)sizeof(sc_stage), "limb staging");
   for (int blk = tid; blk < 32 * MB * KS * 2; blk += DS_NT) {
     const int head = blk / (KS * 2), ks = (blk >> 1) % KS, c = blk & 1;
     const int mb = head >> 5, row = head & 31;
