@@ -186,6 +186,25 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dsa_indexer_topk_decode without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The call allocates nothing: its
+ * scratch is a 40 MiB array in device memory that the library holds on each
+ * device from its load until the process ends, one copy per device, shared
+ * by every call of this entry point on that device.  Calls that overlap in
+ * time on one device race on it (serialise them, e.g. on one stream); a
+ * call needs nothing cleared and leaves its contents behind.  Sizes whose
+ * workspace (dsa_indexer_topk_decode_workspace) exceeds 40 MiB are rejected
+ * with DSA_ERR_UNSUPPORTED before anything is enqueued; B = 32 sequences of
+ * Lmax = 131072 fit.  Arguments, outputs and results as for
+ * dsa_indexer_topk_decode.
+ */
+dsa_status dsa_indexer_topk_decode_noalloc(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                           const float* k_scale, const int32_t* seq_lens,
+                                           int B, int Lmax, int H, int D, int topk,
+                                           int32_t* out_idx, float* out_topk_score, void* stream);
+
+/*
  * Decode over a paged key cache, as serving engines keep it ([IS] 2: the
  * decode indexer scores each sequence's whole cache every step): the same
  * selection as dsa_indexer_topk_decode on the cache the pages describe.

@@ -29,7 +29,8 @@ EXPORTS = (
     "dsa_last_error", "dsa_abi_version",
     "dsa_indexer_topk_prefill_workspace", "dsa_indexer_topk_prefill", "dsa_indexer_topk_prefill_chunk",
     "dsa_indexer_topk_prefill_varlen_workspace", "dsa_indexer_topk_prefill_varlen",
-    "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode", "dsa_indexer_topk_decode_paged",
+    "dsa_indexer_topk_decode_workspace", "dsa_indexer_topk_decode", "dsa_indexer_topk_decode_noalloc",
+    "dsa_indexer_topk_decode_paged",
     "indexcache_resolve", "indexcache_run_layers", "indexcache_run_decode_layers",
     "indexcache_greedy_search", "indexcache_overlap_proxy_loss", "mli_resolve",
     "indexcache_run_decode_layers_mli", "standin_sparse_attention_workspace", "standin_sparse_attention",
@@ -67,6 +68,8 @@ _lib.dsa_indexer_topk_decode_workspace.argtypes = [_i32, _i32, _i32, _i32, _i32,
 _lib.dsa_indexer_topk_decode.restype = _i32
 _lib.dsa_indexer_topk_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                          _vp, _vp, _vp, _sz, _vp]
+_lib.dsa_indexer_topk_decode_noalloc.restype = _i32
+_lib.dsa_indexer_topk_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
 _lib.dsa_indexer_topk_decode_paged.restype = _i32
 _lib.dsa_indexer_topk_decode_paged.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                                _vp, _vp, _vp, _sz, _vp]
@@ -290,6 +293,19 @@ def dsa_indexer_topk_decode(q, w, k_cache, k_scale, seq_lens, topk: int, *, out_
     _check(_lib.dsa_indexer_topk_decode(
         _ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(seq_lens), B, Lmax, H, D, topk,
         _ptr(out_idx), _ptr(out_topk_score), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_idx, out_topk_score
+
+
+def dsa_indexer_topk_decode_noalloc(q, w, k_cache, k_scale, seq_lens, topk: int, out_idx, out_topk_score=None,
+                                    stream=None):
+    """dsa_indexer_topk_decode into caller-provided outputs (out_idx [B,topk]
+    int32, out_topk_score [B,topk] fp32 or None) with the library's
+    per-device scratch: nothing is allocated, here or in the library."""
+    B, H, D = q.shape
+    Lmax = k_cache.shape[1]
+    _check(_lib.dsa_indexer_topk_decode_noalloc(
+        _ptr(q), _ptr(w), _ptr(k_cache), _ptr(k_scale), _ptr(seq_lens), B, Lmax, H, D, topk,
+        _ptr(out_idx), _ptr(out_topk_score), _stream(stream)))
     return out_idx, out_topk_score
 
 

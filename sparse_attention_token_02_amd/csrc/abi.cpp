@@ -409,6 +409,31 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
   return ok();
 }
 
+dsa_status dsa_indexer_topk_decode_noalloc(const uint16_t* q, const uint16_t* w, const uint8_t* k_cache,
+                                           const float* k_scale, const int32_t* seq_lens, int B, int Lmax, int H,
+                                           int D, int topk, int32_t* out_idx, float* out_topk_score,
+                                           void* stream) {
+  if (B < 1 || Lmax < 1 || topk < 1 || topk > kMaxTopk || H < 1 || D < 1)
+    return fail(DSA_ERR_INVALID_ARG, "bad decode sizes B=%d Lmax=%d H=%d D=%d topk=%d", B, Lmax, H, D, topk);
+  if (Lmax > kMaxDecodeLmax || !dsa::decode_supported(H, D, Lmax))
+    return fail(DSA_ERR_UNSUPPORTED, "decode kernels are not built for H=%d D=%d Lmax=%d", H, D, Lmax);
+  const size_t need = decode_ws_bytes(B, Lmax);
+  if (need > dsa::decode_scratch_bytes())
+    return fail(DSA_ERR_UNSUPPORTED,
+                "B=%d x Lmax=%d needs %zu bytes of scratch; the allocation-free decode holds %zu "
+                "(use dsa_indexer_topk_decode with a workspace)", B, Lmax, need, dsa::decode_scratch_bytes());
+  void* scratch = nullptr;
+  const hipError_t e = dsa::decode_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "decode scratch address");
+  DecodeArgs a{q, w, k_cache, k_scale, seq_lens, B, Lmax, H, D, topk, out_idx, out_topk_score, scratch,
+               dsa::decode_scratch_bytes(), static_cast<hipStream_t>(stream)};
+  dsa_status st = validate_decode(a);
+  if (st != DSA_OK) return st;
+  st = launch_decode(a);
+  if (st != DSA_OK) return st;
+  return ok();
+}
+
 dsa_status dsa_indexer_topk_decode_paged(const uint16_t* q, const uint16_t* w, const uint8_t* k_pages,
                                          const float* k_scale_pages, int num_pages, int page_size,
                                          const int32_t* block_table, int max_blocks, const int32_t* seq_lens, int B,

@@ -36,6 +36,8 @@
 // With a paged cache (a block table of pages of 2^n >= 32 keys) each step
 // lies in one page, whose id each wave looks up once, at the start.
 // The kernel boundary orders the phases (no cross-workgroup fences).
+#include <mutex>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -799,6 +801,41 @@ hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_select_kernel, dim3(p.B), dim3(SL_NT), lds, stream, p, score_workgroups(p.Lmax));
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// scratch of the allocation-free decode entry point
+// ---------------------------------------------------------------------------
+
+// One copy per device, held from the library's load to the end of the
+// process; every allocation-free call on a device shares it.
+constexpr size_t DECODE_SCRATCH_BYTES = size_t(40) << 20;
+static __device__ __align__(256) uint8_t scratch[DECODE_SCRATCH_BYTES];
+
+size_t decode_scratch_bytes() { return DECODE_SCRATCH_BYTES; }
+
+// Device address of the current device's copy.  In host code `scratch`
+// names a host-side stand-in, so the address is looked up with
+// hipGetSymbolAddress on a device's first call (that device current) and
+// kept per device.
+hipError_t decode_scratch(void** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace dsa

@@ -122,6 +122,10 @@ bool decode_supported(int H, int D, int Lmax);
 size_t decode_select_lds_bytes(int Lmax);
 DecodeWsSizes decode_ws_sizes(int Lmax);
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream);
+// the allocation-free entry point's per-device scratch: its size, and the
+// current device's address
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 
 // overlap.hip
 size_t overlap_lds_bytes(int N);

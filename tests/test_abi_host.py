@@ -340,3 +340,11 @@ def test_peak_library_exports_its_header():
     assert set(names) == set(peak.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_noalloc_decode_refuses_sizes_beyond_its_scratch_on_the_host():
+    lib = dsa.lib()
+    rc = lib.dsa_indexer_topk_decode_noalloc(None, None, None, None, None, 64, 131072, 64, 128, 2048, None, None,
+                                             None)
+    assert rc == dsa.DSA_ERR_UNSUPPORTED
+    assert b"allocation-free" in lib.dsa_last_error()

@@ -1,0 +1,73 @@
+"""The allocation-free decode entry point (library-held per-device scratch)
+against the workspace entry point, through the C ABI: two calls in a row,
+the second smaller, each bit-identical to dsa_indexer_topk_decode and the
+smaller one also checked against the oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import gen
+from tests import parity
+from tests.gpu_util import dev, host, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_token_02_amd as m
+    return m
+
+
+def _small(seed=3):
+    B, Lmax, H, D = 5, 40000, 64, 128
+    rng = np.random.default_rng(seed)
+    cache, ks = gen.quant_rows_e4m3(rng.standard_normal((B * Lmax, D)).astype(np.float32))
+    q = gen.bf16_bits(rng.standard_normal((B, H, D)).astype(np.float32))
+    w = gen.bf16_bits((rng.standard_normal((B, H)) / 8).astype(np.float32))
+    lens = np.array([40000, 17, 33000, 2048, 20001], dtype=np.int32)
+    return {"cache": cache.reshape(B, Lmax, D), "k_scale": ks.reshape(B, Lmax), "q": q, "w": w, "lens": lens}
+
+
+def test_noalloc_decode_equals_workspace_decode_twice(dsa):
+    import torch
+    from synth.gpu import DeviceGen
+    cfg = gen.CONFIGS["decode_128k"]
+    note("noalloc decode: B=32 x 131072 inputs")
+    big = DeviceGen().decode_inputs(cfg)
+    small_h = _small()
+    small = {k: dev(v) for k, v in small_h.items()}
+    for name, d, topk in (("B=32 x 131072 k=2048", big, cfg["topk"]), ("B=5 x 40000 k=512", small, 512)):
+        B = d["q"].shape[0]
+        note(f"noalloc decode {name}: workspace entry point")
+        ref_i, ref_s = dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk,
+                                                   want_scores=True)
+        oi = torch.full((B, topk), -7, dtype=torch.int32, device="cuda")
+        osc = torch.full((B, topk), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        note(f"noalloc decode {name}: allocation-free entry point")
+        dsa.dsa_indexer_topk_decode_noalloc(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk, oi, osc)
+        torch.cuda.synchronize()
+        assert torch.equal(oi, ref_i), name
+        assert torch.equal(osc.view(torch.int32), ref_s.view(torch.int32)), name
+    res = oracle.decode(small_h["q"], small_h["w"], small_h["cache"], small_h["k_scale"], small_h["lens"], 512,
+                        return_scores=True)
+    M = parity.decode_query_mag(small_h["q"], small_h["w"], small_h["cache"], small_h["k_scale"], small_h["lens"])
+    gi, gs = host(oi), host(osc)
+    for b in range(5):
+        err = parity.check_row(gi[b], res["o"][b], res["A"][b], 512, g_score=gs[b], fmt="fp8q", M=M[b])
+        assert err is None, (b, err)
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch(dsa):
+    lib = dsa.lib()
+    # B=64 x Lmax=131072 needs about 76 MB of scratch: refused on the host, nothing enqueued
+    rc = lib.dsa_indexer_topk_decode_noalloc(None, None, None, None, None, 64, 131072, 64, 128, 2048, None, None,
+                                             None)
+    assert rc == dsa.DSA_ERR_UNSUPPORTED
+    assert b"allocation-free" in lib.dsa_last_error()
