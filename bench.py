@@ -11,8 +11,8 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|prefill_32k_chunked|prefill_ragged|decode_128k_paged|fs_47|
-fs_decode_47|mli_decode_47``)
+(``--workload tiny|prefill_196k|prefill_32k_chunked|prefill_ragged|decode_128k_paged|
+decode_128k_ragged|fs_47|fs_decode_47|mli_decode_47``)
 print their own line.
 """
 from __future__ import annotations
@@ -90,36 +90,141 @@ def time_calls(fn, steps, warmup, stream):
     return [a.elapsed_time(b) for a, b in evs]
 
 
-def cpu_baseline_prefill(cfg, budget_s=12.0):
-    """The fp64 oracle on a seeded sample of query rows of the same workload."""
+def cpu_workers():
+    """Host cores this process may use, at most 16 (one GPU's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _cpu_prefill_worker(job):
+    """One worker of the prefill baseline: the fp64 oracle, BLAS on one
+    thread, over seeded batches of query rows until its time budget is spent
+    (or over the given rows).  Returns (causal pairs, rows, oracle seconds)."""
+    cfg_name, seed, budget_s, fixed_rows = job
     import numpy as np
+    from threadpoolctl import threadpool_limits
     import oracle
     from synth import gen
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    L, H, D, topk = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
-    rng = np.random.default_rng(7)
+    cfg = gen.CONFIGS[cfg_name]
+    L, topk = cfg["L"], cfg["topk"]
     keys = gen.prefill_inputs(cfg, rows=[0])
-    pairs = 0
-    nrows = 0
+    rng = np.random.default_rng(seed)
+    pairs = nrows = 0
     el = 0.0
-    while el < budget_s and nrows < 4096:
-        rows = np.sort(rng.choice(L, size=16, replace=False))
-        inp = gen.prefill_inputs(cfg, rows=rows, with_keys=False)
-        ts = time.perf_counter()
-        oracle.prefill(inp["q"], inp["q_scale"], keys["k"], keys["k_scale"], inp["w"], "fp8", topk, rows=rows)
-        el += time.perf_counter() - ts
-        pairs += int(np.sum(rows + 1))
-        nrows += len(rows)
-    tflops = pairs * 2.0 * H * D / el / 1e12
-    return {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{nrows} seeded query rows of the L={L} prefill ({pairs} causal pairs, fp64 oracle, "
-                      f"{el:.1f} s of oracle time)",
-            "rows_per_s": round(nrows / el, 3),
-            "full_workload_s_extrapolated": round(L * (L + 1) / 2 / (pairs / el), 1)}
+    with threadpool_limits(1):
+        batches = [np.asarray(fixed_rows)] if fixed_rows is not None else None
+        while True:
+            if batches is not None:
+                if not batches:
+                    break
+                rows = batches.pop()
+            else:
+                if el >= budget_s:
+                    break
+                rows = np.sort(rng.choice(L, size=8, replace=False))
+            inp = gen.prefill_inputs(cfg, rows=rows, with_keys=False)
+            ts = time.perf_counter()
+            oracle.prefill(inp["q"], inp["q_scale"], keys["k"], keys["k_scale"], inp["w"], cfg["dtype"], topk,
+                           rows=rows)
+            el += time.perf_counter() - ts
+            pairs += int(np.sum(rows + 1))
+            nrows += len(rows)
+    return pairs, nrows, el
+
+
+def _cpu_decode_worker(job):
+    """One worker of the decode baseline: the fp64 oracle over the given
+    sequences, one at a time (inputs generated outside the timed part).
+    Returns (algorithmic bytes, sequences, oracle seconds)."""
+    cfg_name, seqs = job
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import gen
+    cfg = gen.CONFIGS[cfg_name]
+    H, D, topk = cfg["H"], cfg["D"], cfg["topk"]
+    nbytes = 0.0
+    el = 0.0
+    with threadpool_limits(1):
+        for b in seqs:
+            inp = gen.decode_inputs(cfg, seqs=[b])
+            ts = time.perf_counter()
+            oracle.decode(inp["q"], inp["w"], inp["cache"], inp["k_scale"], inp["lens"], topk)
+            el += time.perf_counter() - ts
+            nbytes += decode_bytes(inp["lens"], H, D, topk, 1)
+    return nbytes, len(seqs), el
+
+
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle as it stands, on the host cores in parallel worker
+    processes (one BLAS thread each), started before anything touches the
+    GPU.  Headline: a seeded row sample of the L=32768 prefill (each worker
+    runs rows for `budget_s` seconds); beside it the whole small prefill
+    (L=2048) and the whole B=32 x 131072 decode."""
+    import multiprocessing as mp
+    import numpy as np
+    from synth import gen
+    nw = cpu_workers()
+    ctx = mp.get_context("spawn")
+    out = {}
+    with ctx.Pool(nw) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_cpu_prefill_worker, [("prefill_32k", 100 + i, budget_s, None) for i in range(nw)])
+        wall = time.perf_counter() - t0
+        pairs = sum(r[0] for r in res)
+        nrows = sum(r[1] for r in res)
+        busy = max(r[2] for r in res)
+        cfg = gen.CONFIGS["prefill_32k"]
+        L, H, D = cfg["L"], cfg["H"], cfg["D"]
+        tflops = pairs * 2.0 * H * D / busy / 1e12
+        out = {"value": round(tflops, 6), "unit": "TFLOP/s", "cores": nw, "kind": "oracle",
+               "sample": f"{nrows} seeded query rows of the L={L} prefill ({pairs} causal pairs) on {nw} worker "
+                         f"processes, {busy:.1f} s of oracle time each (fp64, one BLAS thread per worker)",
+               "rows_per_s": round(nrows / busy, 2),
+               "full_workload_s_extrapolated": round(L * (L + 1) / 2 / (pairs / busy), 1),
+               "wall_s": round(wall, 1)}
+        tcfg = gen.CONFIGS["tiny"]
+        chunks = np.array_split(np.arange(tcfg["L"]), nw)
+        t0 = time.perf_counter()
+        res = pool.map(_cpu_prefill_worker, [("tiny", 0, 0.0, c) for c in chunks if len(c)])
+        wall = time.perf_counter() - t0
+        pairs = sum(r[0] for r in res)
+        tfl = 2.0 * tcfg["H"] * tcfg["D"] * pairs / wall / 1e12
+        out["tiny_full"] = {"value": round(tfl, 6), "unit": "TFLOP/s", "wall_s": round(wall, 2),
+                            "sample": f"the whole L={tcfg['L']} H={tcfg['H']} D={tcfg['D']} bf16 prefill "
+                                      f"(every row), wall time on {nw} workers"}
+        dcfg = gen.CONFIGS["decode_128k"]
+        parts = np.array_split(np.arange(dcfg["B"]), nw)
+        t0 = time.perf_counter()
+        res = pool.map(_cpu_decode_worker, [("decode_128k", [int(b) for b in c]) for c in parts if len(c)])
+        wall = time.perf_counter() - t0
+        nbytes = sum(r[0] for r in res)
+        busy = max(r[2] for r in res)
+        out["decode_128k_full"] = {"value": round(nbytes / busy / 1e9, 4), "unit": "GB/s",
+                                   "us_per_call": round(busy * 1e6, 0),
+                                   "sample": f"the whole B={dcfg['B']} x {dcfg['Lmax']} decode, sequences split "
+                                             f"over {nw} workers; time = the busiest worker's oracle seconds"}
+    return out
+
+
+def measure_peaks(dev):
+    """Measured device peaks on this machine: MFMA-only kernels (fp8, bf16) and
+    HBM read and copy kernels over 2 GiB (libdsa_peak.so)."""
+    import torch
+    from sparse_attention_token_02_amd import peak
+    f8, clk8 = peak.mfma("fp8", iters=5)
+    b16, clk16 = peak.mfma("bf16", iters=5)
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    rd = peak.hbm_read(buf, iters=5)
+    cp = peak.hbm_copy(buf[: 1 << 30], dst, iters=5)
+    del buf, dst
+    torch.cuda.empty_cache()
+    return {"mfma_fp8_tflops": round(f8, 1), "mfma_fp8_clock_mhz": round(clk8, 0),
+            "mfma_bf16_tflops": round(b16, 1), "mfma_bf16_clock_mhz": round(clk16, 0),
+            "hbm_read_gbps": round(rd, 1), "hbm_copy_gbps": round(cp, 1)}
 
 
 def run_main(args):
@@ -200,7 +305,7 @@ def run_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 (fp32 accumulate); decode bf16 x e4m3->bf16",
+        "dtype": "fp8_e4m3 (fp32 accumulate); decode e4m3 keys x bf16 query as two e4m3 limbs",
         "data": "synthetic (seeded, generated on device)",
         "config": {"workload": "prefill L=32768 H=64 D=128 k=2048 fp8 + decode B=32 x 131072 fp8 cache k=2048",
                    "prefill_L": L, "heads": H, "head_dim": D, "topk": topk, "decode_batch": B,
@@ -218,11 +323,14 @@ def run_main(args):
                             "frac": round(dc_gbps / PEAK_HBM_GBPS, 4), "traffic": load_traffic("decode_128k", 1)},
         "kernel_source_hash": kernel_source_hash(),
     }
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle on a row sample)")
-        res["cpu_baseline"] = cpu_baseline_prefill(pcfg, budget_s=args.cpu_budget)
-    else:
-        res["cpu_baseline"] = None
+    log("measured peaks")
+    pk = measure_peaks(dev)
+    res["peaks_measured"] = pk
+    res["roofline"]["peak_measured"] = pk["mfma_fp8_tflops"]
+    res["roofline"]["frac_measured"] = round(pf_tflops / pk["mfma_fp8_tflops"], 4)
+    res["roofline_decode"]["peak_measured"] = pk["hbm_read_gbps"]
+    res["roofline_decode"]["frac_measured"] = round(dc_gbps / pk["hbm_read_gbps"], 4)
+    res["cpu_baseline"] = args.cpu_result
     return res
 
 
@@ -257,6 +365,8 @@ def run_workload(args):
         return run_prefill_ragged(args, g, dsa, gen, stream)
     if name == "decode_128k_paged":
         return run_decode_paged(args, g, dsa, gen, stream)
+    if name == "decode_128k_ragged":
+        return run_decode_ragged(args, g, dsa, gen, stream)
     if name == "prefill_32k_chunked":
         return run_prefill_chunked(args, g, dsa, gen, stream)
     if name == "fs_47":
@@ -301,6 +411,38 @@ def run_decode_paged(args, g, dsa, gen, stream):
                          "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
             "config": {"workload": "decode_128k_paged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
                        "page_size": P}}
+
+
+def run_decode_ragged(args, g, dsa, gen, stream):
+    """The B=32 decode with sequence lengths uniform in [65536, 131072]
+    (seeded), two copies of the cache alternating so that reads come from
+    HBM, as in the main benchmark."""
+    import torch
+    cfg = gen.ragged_decode_config()
+    B, Lmax, H, D, topk = cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"], cfg["topk"]
+    dd = [g.decode_inputs(cfg)]
+    dd.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in dd[0].items()})
+    out = torch.empty((B, topk), dtype=torch.int32, device=g.device)
+    ws = torch.empty(dsa.dsa_indexer_topk_decode_workspace(B, Lmax, H, D, topk), dtype=torch.uint8, device=g.device)
+    turn = [0]
+
+    def call():
+        d = dd[turn[0] & 1]
+        turn[0] += 1
+        dsa.dsa_indexer_topk_decode(d["q"], d["w"], d["cache"], d["k_scale"], d["lens"], topk, out_idx=out,
+                                    workspace=ws, stream=stream)
+
+    ms = time_calls(call, args.steps, args.warmup, stream)
+    avg = sum(ms) / len(ms)
+    lens = gen.decode_lens(cfg)
+    nbytes = decode_bytes(lens, H, D, topk, B)
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    return {"metric": METRIC, "workload": "decode_128k_ragged", "value": round(gbps, 1), "unit": "GB/s",
+            "us_per_call": round(avg * 1e3, 2), "tokens": int(sum(int(n) for n in lens)),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
+            "config": {"workload": "decode_128k_ragged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
+                       "lens": "uniform in [Lmax/2, Lmax], seeded"}}
 
 
 def run_prefill_ragged(args, g, dsa, gen, stream):
@@ -564,6 +706,10 @@ def main():
         print(f"this benchmark runs on one GPU only (asked for --gpus {args.gpus}); the indexer path is measured "
               "per GPU and is not sharded across GPUs", file=sys.stderr)
         sys.exit(2)
+    args.cpu_result = None
+    if args.workload == "main" and not args.no_cpu_baseline:
+        log("cpu baseline (the oracle on the host cores, before the GPU is used)")
+        args.cpu_result = cpu_baseline(budget_s=args.cpu_budget)
     res = run_main(args) if args.workload == "main" else run_workload(args)
     if args.reference_copy_mb > 0:
         import torch

@@ -23,6 +23,8 @@ SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "overlap.hip", "attention.hip
 PEAK_OUT = os.path.join(PKG, "libdsa_peak.so")
 PEAK_SOURCES = ["peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# roctx (per-layer ranges in the schedule drivers), from the ROCm install
+ROCTX_LIBS = ("-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib")
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -45,9 +47,9 @@ def _compile(src: str, obj_dir: str, extra: list[str]) -> str:
     return obj
 
 
-def _link(objs: list[str], out: str) -> str:
+def _link(objs: list[str], out: str, libs: tuple[str, ...] = ()) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs, *libs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -63,7 +65,7 @@ def build(jobs: int = 8, extra: list[str] | None = None, out: str = OUT, peak: b
     srcs = SOURCES + (PEAK_SOURCES if peak else [])
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = dict(zip(srcs, ex.map(lambda s: _compile(s, obj_dir, extra), srcs)))
-    _link([objs[s] for s in SOURCES], out)
+    _link([objs[s] for s in SOURCES], out, ROCTX_LIBS)
     if peak:
         _link([objs[s] for s in PEAK_SOURCES], PEAK_OUT)
     return out

@@ -2,6 +2,7 @@
 // before anything touches HIP), workspace layout, the IndexCache F/S driver
 // and the overlap entry point.  See include/dsa_indexer.h for the contract.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cstdarg>
 #include <algorithm>
@@ -14,6 +15,23 @@
 
 #include "dsa_indexer.h"
 #include "kernels.hpp"
+
+namespace {
+
+// A roctx range around one layer of a schedule ("<schedule> layer <l> <F|S>"),
+// shown by rocprofv3 --marker-trace; a few ns per layer without a profiler.
+struct LayerRange {
+  LayerRange(const char* schedule, int layer, char kind) {
+    char name[96];
+    snprintf(name, sizeof(name), "%s layer %d %c", schedule, layer, kind);
+    roctxRangePushA(name);
+  }
+  ~LayerRange() { roctxRangePop(); }
+  LayerRange(const LayerRange&) = delete;
+  LayerRange& operator=(const LayerRange&) = delete;
+};
+
+}  // namespace
 
 namespace {
 
@@ -42,7 +60,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr size_t kHeader = 256;          // work counter, kept apart from the lists
 constexpr int kMaxSlots = 256;           // persistent workgroups (one per MI355X CU)
-constexpr int kMaxTopk = 4096;
+constexpr int kMaxTopk = dsa::MAX_TOPK;
 constexpr int kMaxDenseL = 16384;
 constexpr int kMaxDecodeLmax = 262144;
 
@@ -501,6 +519,7 @@ dsa_status indexcache_run_layers(const char* pattern, int N, const void* const* 
     }
   }
   for (int l = 0; l < N; ++l) {
+    LayerRange range("indexcache prefill", l, pattern[l]);
     if (pattern[l] == 'F') {
       PrefillArgs a{q[l], q_scale ? q_scale[l] : nullptr, q_scale_head_stride, k[l],
                     k_scale ? k_scale[l] : nullptr, w[l], L, H, D, topk, dt, tcache, nullptr, nullptr,
@@ -543,6 +562,7 @@ dsa_status indexcache_run_decode_layers(const char* pattern, int N, const uint16
     }
   }
   for (int l = 0; l < N; ++l) {
+    LayerRange range("indexcache decode", l, pattern[l]);
     if (pattern[l] == 'F') {
       st = launch_decode(args(l));
       if (st != DSA_OK) {
@@ -655,6 +675,7 @@ dsa_status indexcache_run_decode_layers_mli(const char* pattern, int N, const ui
     return hip_fail(e, "stream fork");
   int waited = -1;   // slot whose completion `stream` already waits for
   for (int l = 0; l < N; ++l) {
+    LayerRange range("mli decode", l, pattern[l]);
     if (pattern[l] == 'F') {
       st = launch_decode(args(l));
       if (st != DSA_OK) {

@@ -142,6 +142,46 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // least 32 keys) lie in one page; lane u of each wave looks up the page of
   // its step u once (nstep <= 64).  Page ids outside [0, num_pages) are
   // clamped into it (no access leaves the page array).
+  // The query block and head weights are loaded first: loads return in
+  // order, so the limb arithmetic below waits only for these, not for the
+  // cache steps issued after them.
+  // Block (head, ks, c) of the query holds the 32 dims
+  // {h HALF + 32 ks + 16 c + i : h < 2, i < 16}, which MFMA step ks reads
+  // from bytes [16c, 16c + 16) of both lane halves; thread blk owns block blk.
+  constexpr int NBLK = 32 * MB * KS * 2;
+  static_assert(NBLK <= DS_NT, "one query block per thread");
+  const int qhead = tid / (KS * 2), qks = (tid >> 1) % KS, qc = tid & 1;
+  v4i qraw[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qraw[h][0] = qraw[h][1] = v4i{0, 0, 0, 0};
+    if (tid < NBLK && qhead < H) {
+      const uint16_t* src = p.q + ((size_t)b * H + qhead) * D + h * HALF + 32 * qks + 16 * qc;
+      qraw[h][0] = *reinterpret_cast<const v4i*>(src);
+      qraw[h][1] = *reinterpret_cast<const v4i*>(src + 8);
+    }
+  }
+  // head weights: result register j of block mb in this lane is head
+  // 32 mb + 8 (j / 4) + 4 kh + j % 4, four consecutive heads per group
+  uint2 wraw[MB][4];
+  const uint16_t* wb = p.w + (size_t)b * H;
+  const bool w8 = (reinterpret_cast<uintptr_t>(p.w) & 7u) == 0;   // 8-byte loads when aligned
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int head0 = 32 * mb + 8 * g + 4 * kh;
+      wraw[mb][g] = make_uint2(0u, 0u);
+      if (head0 < H) {
+        if (w8) {
+          wraw[mb][g] = *reinterpret_cast<const uint2*>(wb + head0);
+        } else {
+          wraw[mb][g] = make_uint2((uint32_t)wb[head0] | ((uint32_t)wb[head0 + 1] << 16),
+                                   (uint32_t)wb[head0 + 2] | ((uint32_t)wb[head0 + 3] << 16));
+        }
+      }
+    }
+
   int step_page = 0;
   if constexpr (PAGED) {
     if (lane < nstep) {
@@ -176,35 +216,25 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
 #pragma unroll
   for (int u = 0; u < DS_PF; ++u) fetch(u, u);
 
-  // ---- the query's limbs.  Block (head, ks, c) holds the 32 dims
-  // {h HALF + 32 ks + 16 c + i : h < 2, i < 16}, which MFMA step ks reads
-  // from bytes [16c, 16c + 16) of both lane halves.  Limb 0 is the block
-  // rounded to e4m3 on the grid of its largest element, limb 1 the exact
-  // residual rounded the same way (a bf16 value has 8 significant bits, a
-  // limb 4).  Staged in operand order, [mb][kk][c][lane][16 bytes] with
-  // kk = limb * KS + ks, and one scale word per (mb, lane): byte kk for lane
-  // (row, c).
+  // ---- the query's limbs.  Limb 0 is the block rounded to e4m3 on the
+  // grid of its largest element, limb 1 the exact residual rounded the same
+  // way (a bf16 value has 8 significant bits, a limb 4).  Staged in operand
+  // order, [mb][kk][c][lane][16 bytes] with kk = limb * KS + ks, and one
+  // scale word per (mb, lane): byte kk for lane (row, c).
   uint8_t* lstage = &ktr[0][0];
   int* lscale = reinterpret_cast<int*>(sc_stage);
   static_assert(MB * NK * 2 * 64 * 16 <= (int)sizeof(ktr) && MB * 64 * 4 <= (int)sizeof(sc_stage), "limb staging");
-  for (int blk = tid; blk < 32 * MB * KS * 2; blk += DS_NT) {
-    const int head = blk / (KS * 2), ks = (blk >> 1) % KS, c = blk & 1;
-    const int mb = head >> 5, row = head & 31;
+  if (tid < NBLK) {
+    const int ks = qks, c = qc;
+    const int mb = qhead >> 5, row = qhead & 31;
     float v[32];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      v4i raw16[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-      if (head < H) {
-        const uint16_t* src = p.q + ((size_t)b * H + head) * D + h * HALF + 32 * ks + 16 * c;
-        raw16[0] = *reinterpret_cast<const v4i*>(src);
-        raw16[1] = *reinterpret_cast<const v4i*>(src + 8);
-      }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t wd = (uint32_t)raw16[i >> 3][(i & 7) >> 1];
+        const uint32_t wd = (uint32_t)qraw[h][i >> 3][(i & 7) >> 1];
         v[16 * h + i] = __uint_as_float((i & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
       }
-    }
 #pragma unroll
     for (int limb = 0; limb < 2; ++limb) {
       float m = 0.f;
@@ -252,14 +282,13 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       qa[mb][kk] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   }
-  // result register j of block mb in this lane is head 32*mb + 8*(j/4) + 4*kh + j%4
   float wr[MB][16];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int head = 32 * mb + 8 * (j >> 2) + 4 * kh + (j & 3);
-      wr[mb][j] = head < H ? bf16_to_f32(p.w[(size_t)b * H + head]) : 0.f;
+      const uint32_t wd = (j & 2) ? wraw[mb][j >> 2].y : wraw[mb][j >> 2].x;
+      wr[mb][j] = __uint_as_float((j & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
     }
   __syncthreads();   // every lane has its operands before scores overwrite the stage
 
@@ -477,6 +506,8 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
   const int nw = (n + 31) >> 5;
   uint32_t* bm = dyn;                  // selected keys
   uint32_t* tb = dyn + nw;             // keys tied with the k-th, later word prefix counts
+  int* obuf = reinterpret_cast<int*>(dyn + 2 * nw);        // the output row, staged
+  float* osbuf = reinterpret_cast<float*>(dyn + 2 * nw + k);
   for (int i = tid; i < nw; i += SL_NT) {
     bm[i] = 0u;
     tb[i] = 0u;
@@ -745,11 +776,17 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
     if ((wbits >> (s & 31)) & 1u) {
       const int pos = (int)tb[s >> 5] + __popc(wbits & ((1u << (s & 31)) - 1u));
       if (pos < k) {
-        out[pos] = s;
-        if (osc) osc[pos] = key_to_float(key);
+        obuf[pos] = s;
+        osbuf[pos] = key_to_float(key);
       }
     }
   });
+  __syncthreads();
+  // exactly k keys are selected: every position is written
+  for (int j = tid; j < k; j += SL_NT) {
+    out[j] = obuf[j];
+    if (osc) osc[j] = osbuf[j];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -758,16 +795,16 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
 
 static int score_workgroups(int Lmax) { return (Lmax + DS_KPB - 1) / DS_KPB; }
 
-size_t decode_select_lds_bytes(int Lmax) {
+size_t decode_select_lds_bytes(int Lmax, int topk) {
   const size_t nw = ((size_t)Lmax + 31) / 32;
-  return 2 * nw * sizeof(uint32_t);
+  return (2 * nw + 2 * (size_t)topk) * sizeof(uint32_t);
 }
 
 bool decode_supported(int H, int D, int Lmax) {
   if (!(H == 16 || H == 32 || H == 64)) return false;
   if (D != 64 && D != 128) return false;
   if (score_workgroups(Lmax) > DS_MAXWG) return false;
-  return decode_select_lds_bytes(Lmax) + sizeof(SelShared) <= 160 * 1024;
+  return decode_select_lds_bytes(Lmax, MAX_TOPK) + sizeof(SelShared) <= 160 * 1024;
 }
 
 DecodeWsSizes decode_ws_sizes(int Lmax) {
@@ -795,7 +832,7 @@ hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream
   else return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = decode_select_lds_bytes(p.Lmax);
+  const size_t lds = decode_select_lds_bytes(p.Lmax, p.topk);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_select_kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -46,6 +46,8 @@ struct PrefillParams {
 hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int nseq, int total_q, int total_k,
                                   int rows_per_item, int4* items, int* n_items, int* counter, hipStream_t stream);
 
+constexpr int MAX_TOPK = 4096;   // the largest k the library accepts
+
 struct DecodeParams {
   const uint16_t* q;         // [B, H, D] bf16
   const uint16_t* w;         // [B, H] bf16
@@ -119,7 +121,7 @@ hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid
 
 // decode.hip
 bool decode_supported(int H, int D, int Lmax);
-size_t decode_select_lds_bytes(int Lmax);
+size_t decode_select_lds_bytes(int Lmax, int topk);
 DecodeWsSizes decode_ws_sizes(int Lmax);
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream);
 // the allocation-free entry point's per-device scratch: its size, and the
