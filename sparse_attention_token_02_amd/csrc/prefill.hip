@@ -635,11 +635,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         float* dsc = p.out_score ? p.out_score + (size_t)(t + qoff) * p.topk : nullptr;
         const int n = sh.row_cnt[row];
         if (n <= lcap_w)
-          wave_select<HCOPIES>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, n, p.topk, dsc, dix, p.topk,
-                               fhist, nullptr, lbuf, lcap_w);
+          wave_select<HCOPIES, true>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, n, p.topk, dsc, dix,
+                                     p.topk, fhist, nullptr, lbuf, lcap_w);
         else
-          wave_select(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, n, p.topk, dsc, dix, p.topk,
-                      sh.whist[wave], nullptr, lbuf, share);
+          wave_select<1, true>(wsc + (size_t)row * p.cap, wix + (size_t)row * p.cap, n, p.topk, dsc, dix, p.topk,
+                               sh.whist[wave], nullptr, lbuf, share);
       }
       break;
     }

@@ -194,7 +194,9 @@ __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int k
 // 4, or null): when the list fits, its scores are copied there once and every
 // later pass reads them from LDS (then dsc must not alias sc).
 // hist: COPIES * 256 words (see wave_find_cut).
-template <int COPIES = 1>
+// STREAM_OUT: the output is final (not read again by this kernel): written
+// with non-temporal stores, so it does not stay behind as dirty cache lines.
+template <int COPIES = 1, bool STREAM_OUT = false>
 __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
                            uint32_t* hist, float* tau, float* lbuf = nullptr, int lcap = 0) {
   const int lane = __lane_id();
@@ -286,8 +288,13 @@ __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if ((take >> e) & 1u) {
-          dix[pos] = iv[u][e];
-          if (dsc) dsc[pos] = sv[u][e];
+          if constexpr (STREAM_OUT) {
+            __builtin_nontemporal_store(iv[u][e], dix + pos);
+            if (dsc) __builtin_nontemporal_store(sv[u][e], dsc + pos);
+          } else {
+            dix[pos] = iv[u][e];
+            if (dsc) dsc[pos] = sv[u][e];
+          }
           ++pos;
         }
       out += __builtin_amdgcn_readlane(nt_incl, 63);
@@ -295,8 +302,13 @@ __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n
     }
   }
   for (int e = out + lane; e < pad_to; e += 64) {
-    dix[e] = -1;
-    if (dsc) dsc[e] = -__builtin_inff();
+    if constexpr (STREAM_OUT) {
+      __builtin_nontemporal_store(-1, dix + e);
+      if (dsc) __builtin_nontemporal_store(-__builtin_inff(), dsc + e);
+    } else {
+      dix[e] = -1;
+      if (dsc) dsc[e] = -__builtin_inff();
+    }
   }
   return out;
 }
