@@ -23,6 +23,10 @@ SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "overlap.hip", "attention.hip
 PEAK_OUT = os.path.join(PKG, "libdsa_peak.so")
 PEAK_SOURCES = ["peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# The decode score kernel's one-lane claims on a shared counter must stay
+# single atomics whose results are read several loads later; the atomic
+# optimizer would turn each into a wave reduction that is waited for at once.
+PER_SOURCE = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 # roctx (per-layer ranges in the schedule drivers), from the ROCm install
 ROCTX_LIBS = ("-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx", "-Wl,-rpath,/opt/rocm/lib")
 ARCH = "gfx950"
@@ -40,7 +44,8 @@ def _compile(src: str, obj_dir: str, extra: list[str]) -> str:
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
     # the host-only C-ABI layer checks caller values (a loss callback) for NaN
     host_only = ["-fhonor-nans"] if src == "abi.cpp" else []
-    cmd = [HIPCC, *COMMON, *host_only, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *host_only, *PER_SOURCE.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -6,6 +6,8 @@
 
 #include <cstdarg>
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -171,13 +173,15 @@ dsa_status launch_prefill(const PrefillArgs& a) {
 // histograms, its list's cut (lowest bin kept, entries) and its list of
 // (key, index) candidates.
 struct DecodeWs {
-  size_t hist, wgcut, cand, total;
+  size_t hdr, hist, wgcut, cand, total;
 };
 
 DecodeWs decode_ws(int B, int Lmax) {
   DecodeWs w{};
   const dsa::DecodeWsSizes z = dsa::decode_ws_sizes(Lmax);
   size_t off = 0;
+  w.hdr = off;   // per-sequence header at a fixed place: its words outlive calls of other sizes
+  off += align_up((size_t)B * sizeof(dsa::DecodeHdr), 256);
   w.hist = off;
   off += align_up((size_t)B * z.hist_words * 4, 256);
   w.wgcut = off;
@@ -189,6 +193,16 @@ DecodeWs decode_ws(int B, int Lmax) {
 }
 
 size_t decode_ws_bytes(int B, int Lmax) { return decode_ws(B, Lmax).total; }
+
+// A fresh 32-bit value per decode launch (SplitMix64 of a process-wide
+// counter started from the clock), for the tag of the sequences' pool counters.
+uint32_t next_nonce() {
+  static std::atomic<uint64_t> ctr{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count()};
+  uint64_t z = ctr.fetch_add(0x9E3779B97F4A7C15ull) + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (uint32_t)(z ^ (z >> 31));
+}
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -237,6 +251,8 @@ dsa_status launch_decode(const DecodeArgs& a) {
   p.out_score = a.out_score;
   uint8_t* base = static_cast<uint8_t*>(a.ws);
   const DecodeWs lay = decode_ws(a.B, a.Lmax);
+  p.hdr = reinterpret_cast<dsa::DecodeHdr*>(base + lay.hdr);
+  p.nonce = next_nonce();
   p.hist = reinterpret_cast<uint32_t*>(base + lay.hist);
   p.wgcut = reinterpret_cast<int2*>(base + lay.wgcut);
   p.cand = reinterpret_cast<uint2*>(base + lay.cand);

@@ -10,8 +10,9 @@
 //
 // Two launches:
 // 1. decode_score_kernel streams the fp8 cache once.  A workgroup owns up to
-//    8192 keys of one sequence (32-key steps interleaved with the other
-//    workgroups of the sequence).  A wave reads 32 whole consecutive keys per
+//    8192 keys of one sequence on average (32-key steps interleaved with the
+//    other workgroups of the sequence, the last quarter claimed from a
+//    shared pool), at most 10240.  A wave reads 32 whole consecutive keys per
 //    step with 16-byte buffer loads (keys past the sequence read as 0 at the
 //    buffer's record limit) and keeps four steps in flight; a per-wave LDS
 //    transpose gives each lane one key column.  The contraction runs on the
@@ -47,18 +48,20 @@ namespace {
 
 constexpr int DS_NT = 256;          // score kernel threads
 constexpr int DS_WAVES = DS_NT / 64;
-constexpr int DS_NSUB = 64;         // 32-key steps per wave
-static_assert(DS_NSUB <= 64, "paged lookup: one lane per step");
+constexpr int DS_NSUB = 64;         // 32-key steps per wave on average (the static map's unit)
+constexpr int DS_CAP = 80;          // 32-key steps a wave can hold (room to take pool chunks)
 constexpr int DS_PF = 4;            // steps in flight per wave
-constexpr int DS_KPB = DS_WAVES * DS_NSUB * 32;   // keys per workgroup
+constexpr int DS_KPB = DS_WAVES * DS_NSUB * 32;   // keys per workgroup on average (sets the grid)
+constexpr int DS_KCAP = DS_WAVES * DS_CAP * 32;   // keys a workgroup can hold
 constexpr int DS_MAXWG = 32;        // score workgroups per sequence at most (Lmax <= 262144)
+constexpr int DS_MAXPOOL = 1024;    // pool chunks per sequence at most, paged cache (pages in LDS)
 constexpr int HBINS = 4096;         // fine bins: top 12 bits of the order-preserving key
 constexpr int CBINS = 256;          // coarse bins: top 8 bits
 constexpr int FPC = HBINS / CBINS;  // fine bins per coarse bin
 constexpr int PW = HBINS / 2 + CBINS / 2;   // words of one score workgroup's packed histograms
 constexpr int SL_NT = 1024;         // select threads
 
-static_assert(DS_KPB < 65536, "16-bit partial histograms");
+static_assert(DS_KCAP < 65536, "16-bit partial histograms");
 static_assert(DS_NT * 16 == HBINS, "score kernel tail: 16 bins per thread");
 
 __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
@@ -77,6 +80,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 template <int KK>
 __device__ __forceinline__ v16f mfma_kk(v8i a, v8i b, v16f c, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, KK, scale_a, 0, 127);
+}
+
+// tag of a call's pool counter: a 32-bit mix of the launch nonce, the
+// sequence's generation word and the sequence index
+__device__ __forceinline__ uint32_t pool_tag(uint32_t nonce, uint32_t gen, int b) {
+  uint32_t h = nonce ^ (gen * 0x9E3779B9u) ^ ((uint32_t)b * 0x85EBCA6Bu);
+  h ^= h >> 16;
+  h *= 0x7FEB352Du;
+  h ^= h >> 15;
+  h *= 0x846CA68Bu;
+  h ^= h >> 16;
+  return h;
+}
+
+__device__ __forceinline__ int score_grid_nwg(int Lmax) { return (Lmax + DS_KPB - 1) / DS_KPB; }
+
+// Workgroup -> (sequence, its workgroup index).  Workgroups go to the 8 XCDs
+// round-robin and fill the CUs in dispatch order, so when nwg is a multiple
+// of 8 the map gives every sequence workgroups on every XCD, early and late
+// in the dispatch order alike (XCD = L % 8; the m-th workgroup of an XCD
+// serves sequence m % B).  Otherwise a sequence's workgroups are consecutive.
+__device__ __forceinline__ void score_block(int L, int B, int nwg, int& b, int& x) {
+  if (nwg % 8 == 0) {
+    const int xcd = L & 7, m = L >> 3;
+    b = m % B;
+    x = (m / B) * 8 + xcd;
+  } else {
+    b = L / nwg;
+    x = L % nwg;
+  }
 }
 
 constexpr float LIMB_MIN = 7.8886091e-31f;     // 2^-100: a smaller block maximum drops the block
@@ -108,20 +141,41 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   __shared__ __attribute__((aligned(16))) uint8_t ktr[DS_WAVES][32 * D];
   // order-preserving keys of the workgroup's scores; at the start, the
   // limbs' scales
-  __shared__ __attribute__((aligned(16))) float sc_stage[DS_KPB];
+  __shared__ __attribute__((aligned(16))) float sc_stage[DS_KCAP];
   __shared__ int sh_cut[2];
+  // the k_scale of the step being scored, per wave (through LDS, so that
+  // the load's register is free again before the next load into it)
+  __shared__ float kst[DS_WAVES][32];
+  // chunk read at each local step of each wave (-1: none), and the number
+  // of steps each wave read, for the tail
+  __shared__ int step_chunk[DS_WAVES][DS_CAP];
+  __shared__ int wave_steps[DS_WAVES];
+  // paged cache: the page of every pool chunk
+  __shared__ int pool_page[PAGED ? DS_MAXPOOL : 1];
 
-  const int b = blockIdx.y;
-  const int len = seq_len(p, b);
-  // Interleaved key mapping: step `sub` of wave w of workgroup x reads the
-  // 32-key chunk (sub * nwg + x) * WAVES + w, so at any moment the workgroups
-  // of a sequence sweep one contiguous region of its cache together.
-  const int nwg = gridDim.x;
-  const int x = blockIdx.x;
+  const int nwg = score_grid_nwg(p.Lmax);
+  int b, x;
+  score_block(blockIdx.x, p.B, nwg, b, x);
+  const int len = __builtin_amdgcn_readfirstlane(seq_len(p, b));   // uniform: scalar descriptors
+  // Interleaved key mapping: static step `sub` of wave w of workgroup x reads
+  // the 32-key chunk (sub * nwg + x) * WAVES + w, so at any moment the
+  // workgroups of a sequence sweep one contiguous region of its cache.
   const int nchunk = (len + 31) >> 5;
   if (DS_WAVES * x >= nchunk) return;     // the select kernel counts only active workgroups
-  // steps this workgroup needs (whole prefetch groups)
-  const int nstep = min(DS_NSUB, ((nchunk - DS_WAVES * x + DS_WAVES * nwg - 1) / (DS_WAVES * nwg) + DS_PF - 1) / DS_PF * DS_PF);
+  // Every wave of the sequence reads its first S steps from the interleaved
+  // static map (S a multiple of the ring depth: about half of the chunks in
+  // all; with a paged cache about 3/4, and at least all but DS_MAXPOOL, whose
+  // pages are looked up in advance); the remaining chunks form a pool that
+  // the waves claim, a ring's worth at a time, from a shared counter once
+  // their static steps are issued, so that waves on slower parts of the
+  // chip, or dispatched later, end no later than the others.  A wave holds
+  // up to DS_CAP steps, more than the average DS_NSUB.
+  constexpr int SNUM = PAGED ? 3 : 1, SDEN = PAGED ? 4 : 2;
+  const int S = max((nchunk * SNUM / SDEN) / (DS_WAVES * nwg) / DS_PF * DS_PF,
+                    PAGED ? (max(nchunk - DS_MAXPOOL, 0) + DS_WAVES * nwg * DS_PF - 1) / (DS_WAVES * nwg * DS_PF) * DS_PF
+                          : 0);
+  const int nstat = S * DS_WAVES * nwg;
+  const int npool = nchunk - nstat;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -129,7 +183,41 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   const int kh = lane >> 5;
   const int col = lane & 31;
 
-  auto chunk_key = [&](int sub) { return 32 * ((sub * nwg + x) * DS_WAVES + wave); };
+  // static step sub < S reads chunk (sub * nwg + x) * WAVES + wave
+  auto static_chunk = [&](int sub) { return (sub * nwg + x) * DS_WAVES + wave; };
+
+  // Pool counter of the sequence: a 64-bit word, claim count in the low
+  // half and, in the high half, the tag of the call that owns it.  The tag
+  // mixes the host's per-launch nonce with the sequence's generation word,
+  // which the select kernel advances after every call, so a word left by an
+  // earlier call (or arbitrary workspace bytes, except with probability
+  // 2^-32) carries another tag; the first claimer that sees one re-tags it
+  // with a compare-and-swap and count 0.  Nothing needs clearing.
+  DecodeHdr* hdr = p.hdr + b;
+  const uint32_t tag = (uint32_t)__builtin_amdgcn_readfirstlane((int)pool_tag(p.nonce, hdr->gen, b));
+  unsigned long long* pool = &hdr->pool;
+  // a claim's old counter value -> the first pool entry of its batch of
+  // DS_PF entries (lane 0 only)
+  auto take = [&](unsigned long long old) -> uint32_t {
+    if ((uint32_t)(old >> 32) != tag) {          // stale: re-tag (rare)
+      bool mine = false;
+      while ((uint32_t)(old >> 32) != tag) {
+        const unsigned long long want = old + DS_PF;   // the claim already added DS_PF
+        const unsigned long long seen =
+            atomicCAS(pool, want, (unsigned long long)tag << 32 | (unsigned long long)DS_PF);
+        if (seen == want) {
+          mine = true;                             // claimed entries 0 .. DS_PF - 1
+          break;
+        }
+        old = atomicAdd(pool, (unsigned long long)DS_PF);
+      }
+      // settle this path's atomics here, so that the register tracking of
+      // the common path does not inherit them as pending
+      __builtin_amdgcn_s_waitcnt(0);
+      if (mine) return 0u;
+    }
+    return (uint32_t)old;
+  };
 
   // cache prefetch ring: step u lives in slot u % DS_PF.  Load i of a step
   // reads bytes [1024 i, 1024 i + 1024) of its 32 keys, 16 per lane (whole
@@ -140,7 +228,8 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   float kss[DS_PF];
   // Paged cache: the 32 keys of a step (s0 a multiple of 32, pages of at
   // least 32 keys) lie in one page; lane u of each wave looks up the page of
-  // its step u once (nstep <= 64).  Page ids outside [0, num_pages) are
+  // its static step u once (at most 56 of them), and the pool chunks' pages
+  // go to LDS.  Page ids outside [0, num_pages) are
   // clamped into it (no access leaves the page array).
   // The query block and head weights are loaded first: loads return in
   // order, so the limb arithmetic below waits only for these, not for the
@@ -184,24 +273,46 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
 
   int step_page = 0;
   if constexpr (PAGED) {
-    if (lane < nstep) {
-      const int sb = min(chunk_key(lane), len - 1);
+    if (lane < S) {
+      const int sb = 32 * static_chunk(lane);
       step_page = p.block_table[(size_t)b * p.max_blocks + (sb >> p.page_shift)];
       step_page = min(max(step_page, 0), p.num_pages - 1);
     }
+    for (int j = tid; j < npool; j += DS_NT) {
+      const int sb = 32 * (nstat + j);
+      const int pg = p.block_table[(size_t)b * p.max_blocks + (sb >> p.page_shift)];
+      pool_page[j] = min(max(pg, 0), p.num_pages - 1);
+    }
   }
+  for (int i = tid; i < DS_WAVES * DS_CAP; i += DS_NT) (&step_chunk[0][0])[i] = -1;
+  // the pool's first claimers are at least a few steps away: one lane of the
+  // sequence's first workgroup tags the counter now, so that claims find it
+  // tagged (a claimer that still finds it stale re-tags it itself)
+  if (x == 0 && tid == 0 && npool > 0) {
+    unsigned long long cur = atomicAdd(pool, 0ull);
+    while ((uint32_t)(cur >> 32) != tag) {
+      const unsigned long long seen = atomicCAS(pool, cur, (unsigned long long)tag << 32);
+      if (seen == cur) break;
+      cur = seen;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();   // pool pages and the step table are in place
   // Each step gets a descriptor based at its first key whose record limit
   // covers only the keys below len (of the page, when paged): the range
   // check then applies to the lane offsets alone.
   const uint8_t* rows_b = p.cache + (size_t)b * p.Lmax * D;
   const float* ks_b = p.k_scale + (size_t)b * p.Lmax;
-  auto fetch = [&](int slot, int sub) {
-    const int s0 = chunk_key(sub);
+  // loads local step `sub` of the wave, chunk c (c < 0: nothing, the loads
+  // read zeros without touching memory)
+  auto fetch = [&](int slot, int sub, int c) {
+    c = __builtin_amdgcn_readfirstlane(c);   // uniform: keeps the descriptors in scalar registers
+    const int s0 = 32 * max(c, 0);
     const uint8_t* rbase = rows_b + (size_t)s0 * D;
     const float* kbase = ks_b + s0;
-    int valid = min(max(len - s0, 0), 32);
+    const int valid = __builtin_amdgcn_readfirstlane(c < 0 ? 0 : min(max(len - s0, 0), 32));
     if constexpr (PAGED) {
-      const int pg = __builtin_amdgcn_readlane(step_page, sub);
+      const int pg = c < 0 ? 0 : sub < S ? __builtin_amdgcn_readlane(step_page, min(sub, 63)) : pool_page[c - nstat];
       const int off = s0 & ((1 << p.page_shift) - 1);
       rbase = p.cache + (((size_t)pg << p.page_shift) + off) * D;
       kbase = p.k_scale + ((size_t)pg << p.page_shift) + off;
@@ -213,8 +324,45 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       raw[slot][i] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rr, 1024 * i + 16 * lane, 0, 0));
     kss[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kr, 4 * col, 0, 0));
   };
+  // Local step u reads chunk cid[u % PF]: a static chunk while u < S, then
+  // pool chunks, a batch of DS_PF consecutive pool entries per ring turn.
+  // The batch for the steps fetched during ring turn g (steps g + PF ..
+  // g + 2 PF - 1) is claimed at the start of turn g - PF and read at the
+  // start of turn g: loads complete in order, so by then it has returned
+  // without an extra wait.
+  int cid[DS_PF];
+  unsigned long long bclm;               // the batch claim in flight (lane 0)
+  bool dry = npool == 0;                 // no pool entry left to claim
+  auto claim = [&]() {                   // only lane 0's value is used
+    if (lane == 0) bclm = atomicAdd(pool, (unsigned long long)DS_PF);
+  };
+  auto batch = [&](unsigned long long v) -> int {   // first pool entry of a batch, or -1 (uniform)
+    int j = 0;
+    if (lane == 0) j = (int)min(take(v), (uint32_t)npool);
+    j = __builtin_amdgcn_readfirstlane(j);
+    if (j >= npool) {
+      dry = true;
+      j = -1;
+    }
+    return j;
+  };
+  // chunk of local step `sub` in a turn whose batch starts at pool entry jb
+  auto chunk_of = [&](int sub, int jb) -> int {
+    if (sub < S) return static_chunk(sub);
+    if (jb < 0 || sub >= DS_CAP) return -1;
+    const int j = jb + (sub & (DS_PF - 1));
+    return j < npool ? nstat + j : -1;
+  };
+  int jb = -1;
+  if (S == 0 && !dry) {                  // the first turn is already pool: claim it now
+    claim();
+    jb = batch(bclm);
+  }
 #pragma unroll
-  for (int u = 0; u < DS_PF; ++u) fetch(u, u);
+  for (int u = 0; u < DS_PF; ++u) cid[u] = chunk_of(u, jb);
+  if (DS_PF >= S && !dry) claim();       // the batch of the next turn, before the first loads
+#pragma unroll
+  for (int u = 0; u < DS_PF; ++u) fetch(u, u, cid[u]);
 
   // ---- the query's limbs.  Limb 0 is the block rounded to e4m3 on the
   // grid of its largest element, limb 1 the exact residual rounded the same
@@ -297,12 +445,18 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   const int rswz = (col / RPB) % CPR;
   // the ring is unrolled inside a rolled loop; with unconditional loads every
   // slot keeps its registers across iterations
+  int nproc = 0;                         // steps read so far (they are the first nproc)
 #pragma unroll 1
-  for (int g = 0; g < nstep; g += DS_PF) {
+  for (int g = 0; g < DS_CAP && cid[0] >= 0; g += DS_PF) {
+    // the batch of the steps this turn fetches, and the claim for the next turn's
+    int jn = -1;
+    if (g + DS_PF >= S && g + DS_PF < DS_CAP && !dry) jn = batch(bclm);
+    if (g + 2 * DS_PF >= S && g + 2 * DS_PF < DS_CAP && !dry) claim();
 #pragma unroll
     for (int u = 0; u < DS_PF; ++u) {
       const int sub = g + u;
-      const int s0 = chunk_key(sub);
+      const int ccur = cid[u];
+      const int s0 = 32 * ccur;
       // through the wave's LDS transpose into per-key operand order
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
@@ -310,13 +464,19 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
         const int r = byte / D, c = (byte % D) / 16;
         *reinterpret_cast<v4i*>(tr + r * D + 16 * (c ^ ((r / RPB) % CPR))) = raw[u][i];
       }
-      const float cks = kss[u];
-      fetch(u, min(sub + DS_PF, nstep - 1));   // past the end: harmless reload
+      if (kh == 0) kst[wave][col] = kss[u];
+      const int nxt = sub + DS_PF;
+      const int cn = chunk_of(nxt, jn);
+      cid[u] = cn;
+      fetch(u, nxt, cn);
+      if (lane == 0 && ccur >= 0) step_chunk[wave][sub] = ccur;
+      if (ccur >= 0) nproc = sub + 1;
       wave_lds_sync();
       v4i cur[NLD];
 #pragma unroll
       for (int i = 0; i < NLD; ++i)
         cur[i] = *reinterpret_cast<const v4i*>(tr + col * D + 16 * ((kh * NLD + i) ^ rswz));
+      const float cks = kst[wave][col];
       wave_lds_sync();   // every lane has read before the next step overwrites
 
       v16f acc[MB];
@@ -344,7 +504,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       tot += __shfl_xor(tot, 32);          // the other half holds the other heads
       const float score = tot * cks;
       const int s = s0 + col;
-      if (kh == 0 && s < len) {
+      if (kh == 0 && ccur >= 0 && s < len) {
         // NaN ranks lowest (a bit test: the library builds with -fno-honor-nans)
         const uint32_t key = (__float_as_uint(score) & 0x7FFFFFFFu) > 0x7F800000u ? 0u : ordered_key(score);
         reinterpret_cast<uint32_t*>(sc_stage)[sub * (32 * DS_WAVES) + wave * 32 + col] = key;
@@ -352,6 +512,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       }
     }
   }
+  if (lane == 0) wave_steps[wave] = nproc;
   __syncthreads();
 
   // ---- tail.  The workgroup's histograms: words [0, HBINS/2) hold the fine
@@ -392,6 +553,10 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   const int incl = wave_incl_sum((int)mine);
   int* wsum = reinterpret_cast<int*>(ktr);     // the transpose area is free now
   if (lane == 63) wsum[wave] = incl;
+  if (tid == 0) {                              // a workgroup whose steps all went to others keeps nothing
+    sh_cut[0] = HBINS;
+    sh_cut[1] = 0;
+  }
   __syncthreads();                             // also: every thread has read its counts
   int higher_waves = 0, total = 0;
 #pragma unroll
@@ -415,19 +580,26 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   }
   __syncthreads();
   const uint32_t dcut = (uint32_t)sh_cut[0];
-  uint2* cand = p.cand + ((size_t)b * nwg + x) * DS_KPB;
+  uint2* cand = p.cand + ((size_t)b * nwg + x) * DS_KCAP;
   // eight keys per thread at a time, so that the LDS reads, the position
   // atomics and the stores of a batch overlap
   constexpr int SCAT = 8;
-  for (int e0 = 0; e0 < nstep * 32 * DS_WAVES; e0 += SCAT * DS_NT) {
+  int nslot = 0;                         // stage slots in use: the longest wave's steps
+#pragma unroll
+  for (int w2 = 0; w2 < DS_WAVES; ++w2) nslot = max(nslot, wave_steps[w2]);
+  nslot *= 32 * DS_WAVES;
+  for (int e0 = 0; e0 < nslot; e0 += SCAT * DS_NT) {
     uint32_t key[SCAT];
     int sidx[SCAT];
 #pragma unroll
     for (int u = 0; u < SCAT; ++u) {
-      const int e = e0 + u * DS_NT + tid;   // past nstep * 128: masked (the LDS read wraps in bounds)
-      const int s = 32 * DS_WAVES * ((e / (32 * DS_WAVES)) * nwg + x) + e % (32 * DS_WAVES);
-      sidx[u] = (e < nstep * 32 * DS_WAVES && s < len) ? s : -1;
-      key[u] = reinterpret_cast<const uint32_t*>(sc_stage)[e & (DS_KPB - 1)];
+      // stage slot: step e / 128, wave (e / 32) % 4, key e % 32 (slots past
+      // nslot are masked; the reads stay in bounds)
+      const int e = min(e0 + u * DS_NT + tid, DS_KCAP - 1);
+      const int c = e0 + u * DS_NT + tid < nslot ? step_chunk[(e >> 5) % DS_WAVES][e / (32 * DS_WAVES)] : -1;
+      const int s = 32 * c + (e & 31);
+      sidx[u] = (c >= 0 && s < len) ? s : -1;
+      key[u] = reinterpret_cast<const uint32_t*>(sc_stage)[e];
     }
     uint32_t pos[SCAT];
 #pragma unroll
@@ -487,8 +659,9 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
   const int k = p.topk;
   int* out = p.out_idx + (size_t)b * k;
   float* osc = p.out_score ? p.out_score + (size_t)b * k : nullptr;
-  const uint2* lists = p.cand + (size_t)b * nwg * DS_KPB;
+  const uint2* lists = p.cand + (size_t)b * nwg * DS_KCAP;
   const uint32_t* ph = p.hist + (size_t)b * nwg * PW;
+  if (tid == 0) p.hdr[b].gen += 1u;   // the next call's pool tag differs from this one's
 
   // A. one round of loads: the length, the lists' cuts and coarse histogram
   //    words (words of lists past the active ones are read but not used)
@@ -542,7 +715,7 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
     __syncthreads();
     for (int i = tid; i < sh.base[nact]; i += SL_NT) {
       const int w = list_of(i);
-      const uint2 c = lists[(size_t)w * DS_KPB + (i - sh.base[w])];
+      const uint2 c = lists[(size_t)w * DS_KCAP + (i - sh.base[w])];
       out[c.y] = (int)c.y;
       if (osc) osc[c.y] = key_to_float(c.x);
     }
@@ -660,7 +833,7 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
     if (i < total) {
       const int w = list_of(i);
       const int e = i - sh.base[w];
-      rc[j] = lists[(size_t)w * DS_KPB + e];
+      rc[j] = lists[(size_t)w * DS_KCAP + e];
       ra[j] = e < sh.gt[w];
     }
   }
@@ -672,7 +845,7 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
     for (int i = tid + SL_NT * SL_REG; i < total; i += SL_NT) {
       const int w = list_of(i);
       const int e = i - sh.base[w];
-      const uint2 c = lists[(size_t)w * DS_KPB + e];
+      const uint2 c = lists[(size_t)w * DS_KCAP + e];
       body(c.x, (int)c.y, e < sh.gt[w]);
     }
   };
@@ -811,13 +984,13 @@ DecodeWsSizes decode_ws_sizes(int Lmax) {
   DecodeWsSizes z;
   z.nwg = (size_t)score_workgroups(Lmax);
   z.hist_words = z.nwg * PW;
-  z.cand_entries = z.nwg * DS_KPB;
+  z.cand_entries = z.nwg * DS_KCAP;
   return z;
 }
 
 template <int H, int D>
 static void launch_score(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(score_workgroups(p.Lmax), p.B);
+  dim3 grid(score_workgroups(p.Lmax) * p.B);
   if (p.block_table) hipLaunchKernelGGL((decode_score_kernel<H, D, true>), grid, dim3(DS_NT), 0, stream, p);
   else hipLaunchKernelGGL((decode_score_kernel<H, D, false>), grid, dim3(DS_NT), 0, stream, p);
 }
@@ -846,7 +1019,7 @@ hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream
 
 // One copy per device, held from the library's load to the end of the
 // process; every allocation-free call on a device shares it.
-constexpr size_t DECODE_SCRATCH_BYTES = size_t(40) << 20;
+constexpr size_t DECODE_SCRATCH_BYTES = size_t(48) << 20;
 static __device__ __align__(256) uint8_t scratch[DECODE_SCRATCH_BYTES];
 
 size_t decode_scratch_bytes() { return DECODE_SCRATCH_BYTES; }

@@ -48,6 +48,15 @@ hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int 
 
 constexpr int MAX_TOPK = 4096;   // the largest k the library accepts
 
+// Per-sequence header of the decode workspace: the pool claim counter
+// (count in the low half, the owning call's tag in the high half) and the
+// generation word that every call's select advances.
+struct DecodeHdr {
+  unsigned long long pool;
+  uint32_t gen;
+  uint32_t pad;
+};
+
 struct DecodeParams {
   const uint16_t* q;         // [B, H, D] bf16
   const uint16_t* w;         // [B, H] bf16
@@ -59,6 +68,8 @@ struct DecodeParams {
   int topk;
   int32_t* out_idx;          // [B, topk]
   float* out_score;          // [B, topk], nullable
+  DecodeHdr* hdr;            // workspace [B]
+  uint32_t nonce;            // per launch, from the host
   uint32_t* hist;            // workspace [B, nwg, PW]: per-workgroup 16-bit histograms
   int2* wgcut;               // workspace [B, nwg]: per list (lowest bin kept, entries)
   uint2* cand;               // workspace [B, nwg, keys per workgroup]: (key, index) lists
