@@ -189,12 +189,12 @@ dsa_status dsa_indexer_topk_decode(const uint16_t* q, const uint16_t* w, const u
  * dsa_indexer_topk_decode without a workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  The call allocates nothing: its
- * scratch is a 40 MiB array in device memory that the library holds on each
+ * scratch is a 48 MiB array in device memory that the library holds on each
  * device from its load until the process ends, one copy per device, shared
  * by every call of this entry point on that device.  Calls that overlap in
  * time on one device race on it (serialise them, e.g. on one stream); a
  * call needs nothing cleared and leaves its contents behind.  Sizes whose
- * workspace (dsa_indexer_topk_decode_workspace) exceeds 40 MiB are rejected
+ * workspace (dsa_indexer_topk_decode_workspace) exceeds 48 MiB are rejected
  * with DSA_ERR_UNSUPPORTED before anything is enqueued; B = 32 sequences of
  * Lmax = 131072 fit.  Arguments, outputs and results as for
  * dsa_indexer_topk_decode.

@@ -66,7 +66,7 @@ def test_noalloc_decode_equals_workspace_decode_twice(dsa):
 
 def test_noalloc_decode_rejects_sizes_beyond_its_scratch(dsa):
     lib = dsa.lib()
-    # B=64 x Lmax=131072 needs about 76 MB of scratch: refused on the host, nothing enqueued
+    # B=64 x Lmax=131072 needs about 93 MB of scratch: refused on the host, nothing enqueued
     rc = lib.dsa_indexer_topk_decode_noalloc(None, None, None, None, None, 64, 131072, 64, 128, 2048, None, None,
                                              None)
     assert rc == dsa.DSA_ERR_UNSUPPORTED
