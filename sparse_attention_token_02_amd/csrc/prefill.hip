@@ -112,6 +112,15 @@ struct PfShared {
   int stage_ix[C::RW][C::TK];
 };
 
+// Dynamic LDS of a launch: the rest of the CU's 160 KB after the static
+// block, less 1 KB of slack (at least the threshold sample's RW x sample_m
+// floats, which are 32 KB at most).  The end-of-item selection uses all of
+// it as scratch for the rows' candidate scores.
+template <int DT, int H, int D>
+constexpr size_t pf_dyn_bytes() {
+  return sizeof(PfShared<DT, H, D>) + 1024 >= 160 * 1024 ? 0 : (160 * 1024 - sizeof(PfShared<DT, H, D>) - 1024) / 1024 * 1024;
+}
+
 template <bool FP8> struct Opnd;
 template <> struct Opnd<true> { typedef v8i T; };
 template <> struct Opnd<false> { typedef v8bf T; };
@@ -611,13 +620,18 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
 
       // ---- final selection: each wave writes its own rows, in ascending key
       // order.  The key tiles, the stage and (when it directly follows the
-      // static block) the sample area are free now: each wave gets an equal,
-      // 16-byte aligned share as scratch for its row's scores.
+      // static block) the dynamic area (the sample and the rest of the LDS)
+      // are free now: each wave gets an equal, 16-byte aligned share as
+      // scratch for its row's scores.
       uint8_t* scr = &sh.ktile[0][0];
       const uint8_t* scr_static_end = reinterpret_cast<const uint8_t*>(&sh.stage_ix[0][0]) + sizeof(sh.stage_ix);
       size_t scr_bytes = (size_t)(scr_static_end - scr);
-      if (reinterpret_cast<const uint8_t*>(dyn_lds) == scr_static_end)
-        scr_bytes += (size_t)C::RW * p.sample_m * sizeof(float);
+      // the dynamic area follows the static block (whose size is padded to
+      // its 1 KB alignment): the span up to its end is this workgroup's LDS
+      const uint8_t* dyn_begin = reinterpret_cast<const uint8_t*>(dyn_lds);
+      const uint8_t* sh_end = reinterpret_cast<const uint8_t*>(&sh) + sizeof(sh);
+      if (dyn_begin >= scr_static_end && dyn_begin <= sh_end + 16)
+        scr_bytes = (size_t)(dyn_begin + pf_dyn_bytes<DT, H, D>() - scr);
       // A row whose list leaves room in the share for a 4-copy digit
       // histogram gets one at the end of the share; a longer list keeps the
       // whole share for its scores and counts into the wave's 1-copy one.
@@ -748,7 +762,8 @@ hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int 
 
 template <int DT, int H, int D, bool DENSE>
 static hipError_t launch_variant(const PrefillParams& p, int grid, hipStream_t stream) {
-  const size_t dyn = (size_t)PfCfg<DT, H, D>::RW * p.sample_m * sizeof(float);
+  const size_t dyn = pf_dyn_bytes<DT, H, D>();
+  if ((size_t)PfCfg<DT, H, D>::RW * p.sample_m * sizeof(float) > dyn) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DT, H, D, DENSE>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
