@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -68,6 +69,21 @@ constexpr int kMaxDecodeLmax = 262144;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Layout checks of the workspaces (region order, alignment, total), built in
+// with -DDSA_DEBUG_BOUNDS (the sanitizer test builds the host code so); a
+// failed check prints where and aborts.
+#ifdef DSA_DEBUG_BOUNDS
+#define DSA_DCHECK(c)                                                                 \
+  do {                                                                                \
+    if (!(c)) {                                                                       \
+      fprintf(stderr, "DSA_DCHECK failed: %s (%s:%d)\n", #c, __FILE__, __LINE__);   \
+      abort();                                                                        \
+    }                                                                                 \
+  } while (0)
+#else
+#define DSA_DCHECK(c) ((void)0)
+#endif
+
 int prefill_cap(int dt, int H, int D, int topk) { return dsa::prefill_list_capacity(dt, H, D, topk); }
 
 int prefill_slots(int L, int H) {
@@ -78,7 +94,10 @@ int prefill_slots(int L, int H) {
 
 size_t prefill_ws_bytes(int L, int H, int D, int topk, dsa_dtype dt) {
   const size_t per = (size_t)dsa::prefill_rows_per_item(H) * prefill_cap((int)dt, H, D, topk);
-  return kHeader + 2 * align_up((size_t)prefill_slots(L, H) * per * 4, 256);
+  const size_t lists = align_up((size_t)prefill_slots(L, H) * per * 4, 256);
+  DSA_DCHECK(per > 0 && prefill_slots(L, H) >= 1 && prefill_slots(L, H) <= kMaxSlots);
+  DSA_DCHECK(kHeader % 256 == 0 && lists >= (size_t)prefill_slots(L, H) * per * 4);
+  return kHeader + 2 * lists;
 }
 
 dsa_status check_prefill_shape(int L, int H, int D, int topk, dsa_dtype dt) {
@@ -189,6 +208,10 @@ DecodeWs decode_ws(int B, int Lmax) {
   w.cand = off;
   off += align_up((size_t)B * z.cand_entries * 8, 256);
   w.total = off;
+  DSA_DCHECK(w.hdr == 0 && w.hdr + (size_t)B * sizeof(dsa::DecodeHdr) <= w.hist);
+  DSA_DCHECK(w.hist % 256 == 0 && w.hist + (size_t)B * z.hist_words * 4 <= w.wgcut);
+  DSA_DCHECK(w.wgcut % 256 == 0 && w.wgcut + (size_t)B * z.nwg * 8 <= w.cand);
+  DSA_DCHECK(w.cand % 256 == 0 && w.cand + (size_t)B * z.cand_entries * 8 <= w.total);
   return w;
 }
 
@@ -349,6 +372,8 @@ static bool varlen_ws(int nseq, int total_q, int H, int D, int topk, dsa_dtype d
   w->lists = w->items + align_up((size_t)w->cap_items * 16, 256);
   const size_t per = (size_t)rw * prefill_cap((int)dt, H, D, topk);
   w->total = w->lists + 2 * align_up((size_t)w->slots * per * 4, 256);
+  DSA_DCHECK(w->items == kHeader && w->items + (size_t)w->cap_items * 16 <= w->lists && w->lists % 256 == 0);
+  DSA_DCHECK(w->slots >= 1 && w->slots <= kMaxSlots && w->lists + 2 * (size_t)w->slots * per * 4 <= w->total);
   return true;
 }
 
