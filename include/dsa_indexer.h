@@ -90,7 +90,9 @@ dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa
  * k        [L, D] dt             keys, one vector per token shared by all heads
  * k_scale  [L] fp32 or NULL (= 1)
  * w        [L, H] bf16           head weights
- * L >= 1; H in {8, 16, 32, 64}; D in {64, 128} (bf16: not H=64 with D=128);
+ * L >= 1; H a multiple of 8 with 8 <= H <= 64 (kernels are built for H in
+ * {8, 16, 32, 64}; other counts run on the next of these with zero heads
+ * appended); D in {64, 128}; bf16 with D=128 needs H <= 32;
  * 1 <= topk <= 4096.
  * out_idx        [L, topk] int32  selected keys, ascending, -1 padded (written in full).
  *                A key whose score is NaN or -inf (finite but extreme inputs can
@@ -175,7 +177,9 @@ dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int 
  * k_cache  [B, Lmax, D] e4m3     indexer key cache
  * k_scale  [B, Lmax] fp32        one scale per cached token
  * seq_lens [B] int32, device     1 <= len_b <= Lmax (read on the device only)
- * B >= 1; H in {16, 32, 64}; D in {64, 128}; 1 <= Lmax <= 262144; 1 <= topk <= 4096.
+ * B >= 1; H a multiple of 8 with 8 <= H <= 64 (run on the kernel built for
+ * the next of {16, 32, 64}, zero heads appended); D in {64, 128};
+ * 1 <= Lmax <= 262144; 1 <= topk <= 4096.
  * out_idx        [B, topk] int32 ascending, -1 padded
  * out_topk_score [B, topk] fp32 or NULL
  */

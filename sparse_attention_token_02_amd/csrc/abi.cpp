@@ -162,6 +162,7 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   p.q = static_cast<const uint8_t*>(a.q);
   p.q_scale = a.q_scale;
   p.qs_row = a.qs_head_stride ? a.H : 1;
+  p.hr = a.H;
   p.qs_head = a.qs_head_stride;
   p.k = static_cast<const uint8_t*>(a.k);
   p.k_scale = a.k_scale;
@@ -264,6 +265,7 @@ dsa_status launch_decode(const DecodeArgs& a) {
   dsa::DecodeParams p{};
   p.q = a.q;
   p.w = a.w;
+  p.hr = a.H;
   p.cache = a.cache;
   p.k_scale = a.k_scale;
   p.lens = a.lens;
@@ -418,6 +420,7 @@ dsa_status dsa_indexer_topk_prefill_varlen(const void* q, const float* q_scale, 
   p.q = static_cast<const uint8_t*>(q);
   p.q_scale = q_scale;
   p.qs_row = q_scale_head_stride ? H : 1;
+  p.hr = H;
   p.qs_head = q_scale_head_stride;
   p.k = static_cast<const uint8_t*>(k);
   p.k_scale = k_scale;

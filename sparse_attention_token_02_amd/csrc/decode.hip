@@ -244,8 +244,8 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     qraw[h][0] = qraw[h][1] = v4i{0, 0, 0, 0};
-    if (tid < NBLK && qhead < H) {
-      const uint16_t* src = p.q + ((size_t)b * H + qhead) * D + h * HALF + 32 * qks + 16 * qc;
+    if (tid < NBLK && qhead < p.hr) {
+      const uint16_t* src = p.q + ((size_t)b * p.hr + qhead) * D + h * HALF + 32 * qks + 16 * qc;
       qraw[h][0] = *reinterpret_cast<const v4i*>(src);
       qraw[h][1] = *reinterpret_cast<const v4i*>(src + 8);
     }
@@ -253,7 +253,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // head weights: result register j of block mb in this lane is head
   // 32 mb + 8 (j / 4) + 4 kh + j % 4, four consecutive heads per group
   uint2 wraw[MB][4];
-  const uint16_t* wb = p.w + (size_t)b * H;
+  const uint16_t* wb = p.w + (size_t)b * p.hr;
   const bool w8 = (reinterpret_cast<uintptr_t>(p.w) & 7u) == 0;   // 8-byte loads when aligned
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
     for (int g = 0; g < 4; ++g) {
       const int head0 = 32 * mb + 8 * g + 4 * kh;
       wraw[mb][g] = make_uint2(0u, 0u);
-      if (head0 < H) {
+      if (head0 < p.hr) {                          // hr is a multiple of 8: all four heads are real
         if (w8) {
           wraw[mb][g] = *reinterpret_cast<const uint2*>(wb + head0);
         } else {
@@ -974,7 +974,7 @@ size_t decode_select_lds_bytes(int Lmax, int topk) {
 }
 
 bool decode_supported(int H, int D, int Lmax) {
-  if (!(H == 16 || H == 32 || H == 64)) return false;
+  if (!decode_head_width(H)) return false;
   if (D != 64 && D != 128) return false;
   if (score_workgroups(Lmax) > DS_MAXWG) return false;
   return decode_select_lds_bytes(Lmax, MAX_TOPK) + sizeof(SelShared) <= 160 * 1024;
@@ -996,6 +996,7 @@ static void launch_score(const DecodeParams& p, hipStream_t stream) {
 }
 
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream) {
+  H = decode_head_width(H);
   if (H == 64 && D == 128) launch_score<64, 128>(p, stream);
   else if (H == 64 && D == 64) launch_score<64, 64>(p, stream);
   else if (H == 32 && D == 128) launch_score<32, 128>(p, stream);

@@ -18,6 +18,7 @@ struct PrefillParams {
   const uint8_t* k;          // [L, D]
   const float* k_scale;      // [L], nullable
   const uint16_t* w;         // [L, H] bf16
+  int hr;                    // H of the caller's q / q_scale / w (the kernel's width pads it)
   int L;                     // keys (query rows are the absolute positions q0 .. L-1)
   int q0;                    // absolute position of query row 0 (0 for a whole sequence)
   int topk;
@@ -48,6 +49,18 @@ hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int 
 
 constexpr int MAX_TOPK = 4096;   // the largest k the library accepts
 
+// Head counts: any multiple of 8 up to 64 runs on the kernels built for the
+// next width in {8, 16, 32, 64} (decode: {16, 32, 64}), the extra heads
+// zero (their dot products, weights and scores contribute nothing).
+inline int prefill_head_width(int H) {
+  if (H < 8 || H > 64 || H % 8) return 0;
+  return H <= 8 ? 8 : H <= 16 ? 16 : H <= 32 ? 32 : 64;
+}
+inline int decode_head_width(int H) {
+  if (H < 8 || H > 64 || H % 8) return 0;
+  return H <= 16 ? 16 : H <= 32 ? 32 : 64;
+}
+
 // Per-sequence header of the decode workspace: the pool claim counter
 // (count in the low half, the owning call's tag in the high half) and the
 // generation word that every call's select advances.
@@ -58,8 +71,9 @@ struct DecodeHdr {
 };
 
 struct DecodeParams {
-  const uint16_t* q;         // [B, H, D] bf16
-  const uint16_t* w;         // [B, H] bf16
+  const uint16_t* q;         // [B, hr, D] bf16
+  const uint16_t* w;         // [B, hr] bf16
+  int hr;                    // the caller's H (the kernel's width pads it with zero heads)
   const uint8_t* cache;      // [B, Lmax, D] e4m3
   const float* k_scale;      // [B, Lmax]
   const int32_t* lens;       // [B] device

@@ -219,8 +219,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
         const int head = HSTRIDE * mb + a_head;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          if (t < L) {
-            const uint8_t* src = p.q + ((size_t)(t + qoff) * H + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
+          if (t < L && head < p.hr) {
+            const uint8_t* src = p.q + ((size_t)(t + qoff) * p.hr + head) * C::ROWB + kh * (C::ROWB / 2) + ks * C::SB;
             qa[mb][ks] = load_opnd<C::FP8>(src);
           } else {
             qa[mb][ks] = zero_opnd<C::FP8>();
@@ -233,8 +233,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
     for (int i = tid; i < C::RW * H; i += NT) {
       const int t = t0 + i / H, head = i % H;
       float v = 0.f;
-      if (t < L) {
-        v = bf16_to_f32(p.w[(size_t)(t + qoff) * H + head]);
+      if (t < L && head < p.hr) {
+        v = bf16_to_f32(p.w[(size_t)(t + qoff) * p.hr + head]);
         if (p.q_scale) v *= p.q_scale[(size_t)(t + qoff) * p.qs_row + (size_t)head * p.qs_head];
       }
       sh.weff[i] = v;
@@ -800,11 +800,14 @@ static bool pf_info(int dt, int H, int D, PfInfo* out) {
   return false;
 }
 
-int prefill_rows_per_item(int H) { return H >= 32 ? WAVES : WAVES * 2 * (16 / H); }
+int prefill_rows_per_item(int H) {
+  H = prefill_head_width(H);
+  return H >= 32 ? WAVES : WAVES * 2 * (16 / H);
+}
 
 bool prefill_supported(int dt, int H, int D) {
   PfInfo info;
-  return pf_info(dt, H, D, &info);
+  return prefill_head_width(H) && pf_info(dt, prefill_head_width(H), D, &info);
 }
 
 // Keys per row sampled for the threshold estimate: the sampled scores of all
@@ -813,7 +816,7 @@ bool prefill_supported(int dt, int H, int D) {
 // the sample.
 int prefill_sample_keys(int dt, int H, int D) {
   PfInfo info;
-  if (!pf_info(dt, H, D, &info)) return 0;
+  if (!pf_info(dt, prefill_head_width(H), D, &info)) return 0;
   const size_t lds_limit = 160 * 1024;
   const int tk = info.tile_keys;
   const int rw = prefill_rows_per_item(H);
@@ -830,7 +833,7 @@ int prefill_sample_keys(int dt, int H, int D) {
 // configuration is not built.
 int prefill_list_capacity(int dt, int H, int D, int topk) {
   PfInfo info;
-  if (!pf_info(dt, H, D, &info)) return 0;
+  if (!pf_info(dt, prefill_head_width(H), D, &info)) return 0;
   const size_t tk = (size_t)info.tile_keys;
   size_t cap = 4 * (size_t)topk;
   if (cap < (size_t)topk + 16 * tk) cap = (size_t)topk + 16 * tk;
@@ -843,6 +846,7 @@ hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid
   const long long n_dense = p.out_dense ? (long long)(p.L - p.q0) * p.L : 0;
   const int pg = n_dense ? 1024 : 1;
   hipLaunchKernelGGL(prefill_prepare_kernel, dim3(pg), dim3(256), 0, stream, p.counter, p.out_dense, n_dense);
+  H = prefill_head_width(H);
 #define DSA_PF_CASE(DT_, H_, D_) \
   if (dt == DT_ && H == H_ && D == D_) return launch_one<DT_, H_, D_>(p, grid, stream);
   DSA_PF_CONFIGS(DSA_PF_CASE)

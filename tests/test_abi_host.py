@@ -74,13 +74,20 @@ def test_prefill_workspace_query():
     for args, st in [((0, 64, 128, 2048, "fp8"), dsa.DSA_ERR_INVALID_ARG),
                      ((1024, 64, 128, 0, "fp8"), dsa.DSA_ERR_INVALID_ARG),
                      ((1024, 64, 128, 5000, "fp8"), dsa.DSA_ERR_INVALID_ARG),
-                     ((1024, 48, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
+                     ((1024, 44, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
+                     ((1024, 72, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
+                     ((1024, 48, 128, 64, "bf16"), dsa.DSA_ERR_UNSUPPORTED),
                      ((1024, 64, 96, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
                      ((1024, 128, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
                      ((1024, 64, 128, 64, "bf16"), dsa.DSA_ERR_UNSUPPORTED)]:
         with pytest.raises(dsa.DsaError) as e:
             dsa.dsa_indexer_topk_prefill_workspace(*args)
         assert e.value.status == st, args
+    # a head count between the built widths takes the next width's layout
+    assert dsa.dsa_indexer_topk_prefill_workspace(1024, 48, 128, 64, "fp8") == \
+        dsa.dsa_indexer_topk_prefill_workspace(1024, 64, 128, 64, "fp8")
+    assert dsa.dsa_indexer_topk_prefill_workspace(1024, 24, 64, 64, "bf16") == \
+        dsa.dsa_indexer_topk_prefill_workspace(1024, 32, 64, 64, "bf16")
     lib = dsa.lib()
     assert lib.dsa_indexer_topk_prefill_workspace(16, 8, 64, 4, 7, ctypes.byref(ctypes.c_size_t())) == \
         dsa.DSA_ERR_INVALID_ARG
@@ -158,7 +165,8 @@ def test_decode_rejects_before_any_device_call():
                                            a["D"], a["topk"], a["oi"], a["osc"], a["ws"], a["wsb"], None)
     assert call(lens=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(B=0) == dsa.DSA_ERR_INVALID_ARG
-    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
     assert call(Lmax=1 << 20) == dsa.DSA_ERR_UNSUPPORTED
     assert call(wsb=100) == dsa.DSA_ERR_WORKSPACE
     assert call(c=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG
@@ -175,7 +183,8 @@ def test_decode_paged_rejects_before_any_device_call():
     assert call(npages=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(table=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(mb=8193) == dsa.DSA_ERR_UNSUPPORTED          # more than 262144 tokens
-    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
     assert call(wsb=64) == dsa.DSA_ERR_WORKSPACE
     assert call(c=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG
 
@@ -233,7 +242,8 @@ def test_run_decode_layers_rejects_before_any_device_call():
     assert call(tc=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
     assert "layer 0" in dsa.dsa_last_error()
-    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
     assert call(qq=arr(FAKE, FAKE, None)) == dsa.DSA_ERR_INVALID_ARG     # layer 2 is F and has no q
     assert "layer 2" in dsa.dsa_last_error()
     assert call(cache=arr(FAKE, FAKE, FAKE + 8)) == dsa.DSA_ERR_INVALID_ARG   # misaligned cache of layer 2
@@ -263,7 +273,8 @@ def test_run_decode_layers_mli_rejects_before_any_device_call():
     assert call(sb=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
     assert "layer 0" in dsa.dsa_last_error()
-    assert call(H=8) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
     assert call(qq=P(FAKE, FAKE, None)) == dsa.DSA_ERR_INVALID_ARG
     assert "layer 2" in dsa.dsa_last_error()
 

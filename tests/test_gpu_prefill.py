@@ -192,6 +192,23 @@ def test_every_built_configuration(dsa, dt, H, D):
     _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk, fmt=dt)
 
 
+@pytest.mark.parametrize("dt,H,D", [("fp8", 24, 128), ("fp8", 40, 64), ("fp8", 56, 128), ("bf16", 24, 64),
+                                     ("bf16", 48, 64)])
+def test_head_counts_between_the_built_widths(dsa, dt, H, D):
+    """H a multiple of 8 that no kernel is built for runs on the next
+    built width with zero heads appended; the caller's [L, H, D] layout is
+    read as it is."""
+    L, topk = 1109, 96
+    cfg = dict(kind="prefill", L=L, H=H, D=D, topk=topk, dtype=dt, seed=5 * H + D + (dt == "bf16"),
+               heavy_count=11, heavy_factor=3.0, qk_div=8.0, w_div=8.0)
+    note(f"prefill padded head count {dt} H={H} D={D} L={L} k={topk}")
+    inp = gen.prefill_inputs(cfg)
+    idx, sc, _ = _run(dsa, inp, cfg, want_scores=True)
+    check_structure_all(idx, topk)
+    rows = sample_rows(L, topk, 48, seed=H * D + 1)
+    _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk, fmt=dt)
+
+
 @pytest.mark.parametrize("dt,H,D", BUILT)
 def test_every_built_configuration_with_key_sample(dsa, dt, H, D):
     """L=5003, k=64: work items from position 2048 (128-key tiles) or 4096
