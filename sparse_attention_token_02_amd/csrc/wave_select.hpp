@@ -196,6 +196,10 @@ __device__ __forceinline__ uint32_t wave_kth_key(const float* vals, int n, int k
 // hist: COPIES * 256 words (see wave_find_cut).
 // STREAM_OUT: the output is final (not read again by this kernel): written
 // with non-temporal stores, so it does not stay behind as dirty cache lines.
+// When lbuf can hold the min(n, k) kept indices, they are gathered there
+// first (at their output positions, all of which precede the entries still
+// to be read) and written out with whole-line stores at the end; scattered
+// non-temporal stores would reach HBM as partial lines, several per line.
 template <int COPIES = 1, bool STREAM_OUT = false>
 __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n, int k, float* dsc, int* dix, int pad_to,
                            uint32_t* hist, float* tau, float* lbuf = nullptr, int lcap = 0) {
@@ -236,6 +240,9 @@ __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n
   }
   if (n > k) cut = wave_find_cut<COPIES>(ksc, n, k, hist, tau != nullptr, have_lo_hi ? lo_hi : nullptr);
   if (tau) *tau = n > k ? key_to_float(cut.kth) : -__builtin_inff();
+  int* ob = nullptr;                      // staged output indices (STREAM_OUT)
+  if constexpr (STREAM_OUT)
+    if (lbuf && min(n, k) <= lcap) ob = reinterpret_cast<int*>(lbuf);
   int out = 0;
   uint32_t eq_seen = 0;
   constexpr int U = 4;                    // float4 groups per lane and batch
@@ -289,7 +296,8 @@ __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n
       for (int e = 0; e < 4; ++e)
         if ((take >> e) & 1u) {
           if constexpr (STREAM_OUT) {
-            __builtin_nontemporal_store(iv[u][e], dix + pos);
+            if (ob) ob[pos] = iv[u][e];
+            else __builtin_nontemporal_store(iv[u][e], dix + pos);
             if (dsc) __builtin_nontemporal_store(sv[u][e], dsc + pos);
           } else {
             dix[pos] = iv[u][e];
@@ -301,9 +309,19 @@ __device__ __forceinline__ int wave_select(const float* sc, const int* ix, int n
       eq_seen += (uint32_t)__builtin_amdgcn_readlane(eq_incl, 63);
     }
   }
+  if constexpr (STREAM_OUT) {
+    if (ob) {
+      // the row from the 256-byte boundary at or below dix: each store
+      // instruction covers one aligned 256-byte block
+      wave_lds_sync();
+      const int b0 = -(int)((reinterpret_cast<uintptr_t>(dix) >> 2) & 63);
+      for (int e = b0 + lane; e < pad_to; e += 64)
+        if (e >= 0) __builtin_nontemporal_store(e < out ? ob[e] : -1, dix + e);
+    }
+  }
   for (int e = out + lane; e < pad_to; e += 64) {
     if constexpr (STREAM_OUT) {
-      __builtin_nontemporal_store(-1, dix + e);
+      if (!ob) __builtin_nontemporal_store(-1, dix + e);
       if (dsc) __builtin_nontemporal_store(-__builtin_inff(), dsc + e);
     } else {
       dix[e] = -1;
