@@ -167,6 +167,7 @@ def test_decode_rejects_before_any_device_call():
     assert call(B=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
     assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=128) == dsa.DSA_ERR_UNSUPPORTED             # out on purpose: the register budget
     assert call(Lmax=1 << 20) == dsa.DSA_ERR_UNSUPPORTED
     assert call(wsb=100) == dsa.DSA_ERR_WORKSPACE
     assert call(c=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG
