@@ -176,7 +176,10 @@ dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int 
  * w        [B, H] bf16           head weights
  * k_cache  [B, Lmax, D] e4m3     indexer key cache
  * k_scale  [B, Lmax] fp32        one scale per cached token
- * seq_lens [B] int32, device     1 <= len_b <= Lmax (read on the device only)
+ * seq_lens [B] int32, device     1 <= len_b <= Lmax (read on the device only, so
+ *                                not checked: a value outside [0, Lmax] is clamped
+ *                                into it, and a length of 0 gives a row of -1 with
+ *                                -inf scores)
  * B >= 1; H a multiple of 8 with 8 <= H <= 64 (run on the kernel built for
  * the next of {16, 32, 64}, zero heads appended); D in {64, 128};
  * 1 <= Lmax <= 262144; 1 <= topk <= 4096.

@@ -62,6 +62,31 @@ def test_decode_odd_cache_length(dsa):
     _compare(idx, sc, inp, 2048)
 
 
+def test_decode_lengths_outside_the_cache_are_clamped(dsa):
+    """Lengths are read on the device, so they cannot be rejected on the host:
+    a length of 0 or below is an empty cache (a row of -1 with -inf scores),
+    and a length above Lmax reads Lmax keys."""
+    Lmax, topk = 3000, 512
+    lens = [0, 2000, -7, Lmax + 50, 1]
+    inp = _small_inputs(5, Lmax, 64, 128, lens, seed=21)
+    note("decode lengths 0, negative and above Lmax")
+    idx, sc = _run(dsa, inp, topk)
+    for b in (0, 2):
+        assert np.all(idx[b] == -1) and np.all(np.isneginf(sc[b])), b
+    clamped = dict(inp, lens=np.clip(inp["lens"], 0, Lmax).astype(np.int32))
+    _compare(idx, sc, clamped, topk, seqs=[1, 3, 4])
+
+
+def test_decode_longest_cache(dsa):
+    """Lmax = 262144, the longest cache the score grid covers (32 workgroups
+    per sequence): a full sequence and a ragged one against the oracle."""
+    Lmax, topk = 262144, 2048
+    inp = _small_inputs(2, Lmax, 64, 128, [Lmax, 200001], seed=23)
+    note("decode Lmax=262144")
+    idx, sc = _run(dsa, inp, topk)
+    _compare(idx, sc, inp, topk)
+
+
 def test_decode_one_giant_tie_takes_lowest_indices(dsa):
     """q = 0: every score is 0, the threshold bin holds every key (more than fit
     in the candidate buffer), and the selection must be keys 0..k-1."""

@@ -239,6 +239,21 @@ def test_topk_limits(dsa, L, topk):
     _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk)
 
 
+@pytest.mark.parametrize("L", [1, 2, 3])
+def test_shortest_sequences_select_every_key(dsa, L):
+    """L <= k: every row keeps all of its keys 0..t, in order, -1 padded."""
+    topk = 2048
+    cfg = dict(gen.CONFIGS["prefill_32k"], L=L, topk=topk, heavy_count=0)
+    note(f"prefill L={L}")
+    inp = gen.prefill_inputs(cfg)
+    idx, sc, _ = _run(dsa, inp, cfg, want_scores=True)
+    idx, sc = host(idx), host(sc)
+    for t in range(L):
+        assert idx[t].tolist() == list(range(t + 1)) + [-1] * (topk - t - 1), t
+    rows = np.arange(L)
+    _compare(idx, sc, _oracle_rows(inp, cfg, rows), rows, topk)
+
+
 def test_overflowing_scores_still_write_every_row(dsa):
     """Finite but extreme head weights on some rows overflow their scores to
     inf and NaN (mixed signs).  A NaN or -inf score is never selected, so
