@@ -98,6 +98,10 @@ dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa
  *                A key whose score is NaN or -inf (finite but extreme inputs can
  *                overflow) is never selected; its row then holds fewer than
  *                min(topk, t+1) keys and is padded, still written in full.
+ *                When neither scores nor dense scores are requested, rows with
+ *                t + 1 <= topk may be answered without scoring them: every key
+ *                0 .. t is then selected, whatever its score (with finite scores,
+ *                the same selection).
  * out_topk_score [L, topk] fp32   scores aligned with out_idx, -inf padded; NULL to skip
  * out_dense_score [L, L] fp32     every score, -inf above the diagonal; NULL to skip;
  *                                 only for L <= 16384 (a debugging aid: the normal path

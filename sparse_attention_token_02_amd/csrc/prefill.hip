@@ -207,6 +207,18 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
       L = p.L;
       t0 = p.q0 + (p.n_items - 1 - item) * C::RW;
     }
+    // Every row of the item has at most topk keys: its selection is all of
+    // them, 0 .. t in order.  Without requested scores nothing needs scoring.
+    if (!DENSE && p.out_score == nullptr && t0 + C::RW <= p.topk) {
+      for (int rl = wave; rl < C::RW; rl += WAVES) {
+        const int t = t0 + rl;
+        if (t >= L) break;
+        int* dix = p.out_idx + (size_t)(t + qoff) * p.topk;
+        for (int j = lane; j < p.topk; j += 64) __builtin_nontemporal_store(j <= t ? j : -1, dix + j);
+      }
+      __syncthreads();   // every thread has read sh.item before the next one is taken
+      continue;
+    }
     const int kend = min(t0 + C::RW, L);
     const int ntiles = (kend + C::TK - 1) / C::TK;
 

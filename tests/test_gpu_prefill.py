@@ -227,6 +227,25 @@ def test_every_built_configuration_with_key_sample(dsa, dt, H, D):
     _compare(host(idx), host(sc), _oracle_rows(inp, cfg, rows), rows, topk, fmt=dt)
 
 
+@pytest.mark.parametrize("dt,H,D,L,topk", [("fp8", 64, 128, 5003, 2048), ("bf16", 16, 64, 1109, 256),
+                                          ("fp8", 8, 128, 700, 100)])
+def test_without_scores_equals_with_scores(dsa, dt, H, D, L, topk):
+    """Without requested scores, a work item whose rows all have t + 1 <= topk
+    is answered without scoring: each row keeps every key 0..t.  With finite
+    scores that is the selection the scoring path makes, so every row of the
+    call equals the call that also returns scores."""
+    cfg = dict(kind="prefill", L=L, H=H, D=D, topk=topk, dtype=dt, seed=7 * H + D + (dt == "bf16"),
+               heavy_count=L // 100, heavy_factor=3.0, qk_div=8.0, w_div=8.0)
+    note(f"prefill without scores {dt} H={H} D={D} L={L} k={topk}")
+    inp = gen.prefill_inputs(cfg)
+    plain, _, _ = _run(dsa, inp, cfg)
+    with_sc, _, _ = _run(dsa, inp, cfg, want_scores=True)
+    plain, with_sc = host(plain), host(with_sc)
+    assert np.array_equal(plain, with_sc)
+    for t in range(min(L, topk)):
+        assert plain[t, :t + 1].tolist() == list(range(t + 1)) and np.all(plain[t, t + 1:] == -1), t
+
+
 @pytest.mark.parametrize("L,topk", [(700, 1), (5003, 4096)])
 def test_topk_limits(dsa, L, topk):
     """The smallest k and the largest the library accepts."""

@@ -117,6 +117,12 @@ def test_varlen_batch_equals_per_sequence_calls(dsa):
     idx, sc = dsa.dsa_indexer_topk_prefill_varlen(dev(q), dev(qs), dev(k), dev(ks), dev(w), dev(cu_q), dev(cu_k),
                                                   topk, "fp8", out_idx=idx, want_scores=True)
     torch.cuda.synchronize()
+    # without scores (items of rows with t + 1 <= topk are then not scored): the same indices
+    plain = torch.full((len(q), topk), -7, dtype=torch.int32, device="cuda")
+    plain, _ = dsa.dsa_indexer_topk_prefill_varlen(dev(q), dev(qs), dev(k), dev(ks), dev(w), dev(cu_q), dev(cu_k),
+                                                   topk, "fp8", out_idx=plain)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, idx)
     for i, (lq, lk) in enumerate(seqs):
         if lq == 0:
             continue
