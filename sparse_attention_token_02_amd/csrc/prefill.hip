@@ -44,6 +44,8 @@
 //   row and writes them out in order.
 // * Persistent grid: one workgroup per CU pulls work items from an atomic
 //   counter, longest (highest t) first, which balances the causal triangle.
+//   A work item whose rows all have t + 1 <= k keeps every key; when the
+//   caller wants no scores it is written out without being scored.
 // * Query rows need not start at position 0: a chunk (query offset q0) or a
 //   ragged batch (a device table of items, each naming its sequence's key
 //   rows, key count, q row offset and first position) reads its rows at
