@@ -596,7 +596,8 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       // stage slot: step e / 128, wave (e / 32) % 4, key e % 32 (slots past
       // nslot are masked; the reads stay in bounds)
       const int e = min(e0 + u * DS_NT + tid, DS_KCAP - 1);
-      const int c = e0 + u * DS_NT + tid < nslot ? step_chunk[(e >> 5) % DS_WAVES][e / (32 * DS_WAVES)] : -1;
+      const int cr = step_chunk[(e >> 5) % DS_WAVES][e / (32 * DS_WAVES)];   // read unconditionally: no branch
+      const int c = e0 + u * DS_NT + tid < nslot ? cr : -1;
       const int s = 32 * c + (e & 31);
       sidx[u] = (c >= 0 && s < len) ? s : -1;
       key[u] = reinterpret_cast<const uint32_t*>(sc_stage)[e];
