@@ -135,6 +135,35 @@ def _cpu_prefill_worker(job):
     return pairs, nrows, el
 
 
+def _cpu_fs_worker(job):
+    """One worker of the layer-reuse baseline: the fp64 oracle on seeded
+    batches of query rows of one layer of the 47-layer workload, until its
+    time budget is spent (the layer's keys are built outside the timed part).
+    Returns (causal pairs, rows, oracle seconds)."""
+    layer, seed, budget_s = job
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from synth import gen
+    cfg = gen.CONFIGS["fs_47"]
+    L, topk = cfg["L"], cfg["topk"]
+    keys = gen.fs_layer_inputs(cfg, layer, rows=[0])
+    rng = np.random.default_rng(seed)
+    pairs = nrows = 0
+    el = 0.0
+    with threadpool_limits(1):
+        while el < budget_s:
+            rows = np.sort(rng.choice(L, size=8, replace=False))
+            inp = gen.fs_layer_inputs(cfg, layer, rows=rows, with_keys=False)
+            ts = time.perf_counter()
+            oracle.prefill(inp["q"], inp["q_scale"], keys["k"], keys["k_scale"], inp["w"], cfg["dtype"], topk,
+                           rows=rows)
+            el += time.perf_counter() - ts
+            pairs += int(np.sum(rows + 1))
+            nrows += len(rows)
+    return pairs, nrows, el
+
+
 def _cpu_decode_worker(job):
     """One worker of the decode baseline: the fp64 oracle over the given
     sequences, one at a time (inputs generated outside the timed part).
@@ -155,6 +184,40 @@ def _cpu_decode_worker(job):
             el += time.perf_counter() - ts
             nbytes += decode_bytes(inp["lens"], H, D, topk, 1)
     return nbytes, len(seqs), el
+
+
+def cpu_baseline_workload(name, budget_s=12.0):
+    """The fp64 oracle on a seeded row sample of a secondary prefill workload,
+    on the host cores in worker processes: L=196608 (rows of the one
+    sequence) or the 47-layer workload (rows of every third layer, one layer
+    per worker).  None for the other workloads."""
+    import multiprocessing as mp
+    from synth import gen
+    nw = cpu_workers()
+    ctx = mp.get_context("spawn")
+    if name == "prefill_196k":
+        jobs, worker, layers = [("prefill_196k", 100 + i, budget_s, None) for i in range(nw)], _cpu_prefill_worker, 1
+        cfg = gen.CONFIGS["prefill_196k"]
+    elif name == "fs_47":
+        cfg = gen.CONFIGS["fs_47"]
+        jobs, worker, layers = [((3 * i) % cfg["N"], 100 + i, budget_s) for i in range(nw)], _cpu_fs_worker, cfg["N"]
+    else:
+        return None
+    with ctx.Pool(nw) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(worker, jobs)
+        wall = time.perf_counter() - t0
+    pairs = sum(r[0] for r in res)
+    nrows = sum(r[1] for r in res)
+    busy = max(r[2] for r in res)
+    L, H, D = cfg["L"], cfg["H"], cfg["D"]
+    what = f"L={L}" if layers == 1 else f"{layers}-layer L={L}"
+    return {"value": round(pairs * 2.0 * H * D / busy / 1e12, 6), "unit": "TFLOP/s", "cores": nw, "kind": "oracle",
+            "sample": f"{nrows} seeded query rows of the {what} prefill ({pairs} causal pairs) on {nw} worker "
+                      f"processes, {busy:.1f} s of oracle time each (fp64, one BLAS thread per worker)",
+            "rows_per_s": round(nrows / busy, 2),
+            "full_workload_s_extrapolated": round(layers * L * (L + 1) / 2 / (pairs / busy), 1),
+            "wall_s": round(wall, 1)}
 
 
 def cpu_baseline(budget_s=12.0):
@@ -707,10 +770,16 @@ def main():
               "per GPU and is not sharded across GPUs", file=sys.stderr)
         sys.exit(2)
     args.cpu_result = None
-    if args.workload == "main" and not args.no_cpu_baseline:
-        log("cpu baseline (the oracle on the host cores, before the GPU is used)")
-        args.cpu_result = cpu_baseline(budget_s=args.cpu_budget)
+    if not args.no_cpu_baseline:
+        if args.workload == "main":
+            log("cpu baseline (the oracle on the host cores, before the GPU is used)")
+            args.cpu_result = cpu_baseline(budget_s=args.cpu_budget)
+        elif args.workload in ("prefill_196k", "fs_47"):
+            log("cpu baseline of the workload (the oracle on the host cores, before the GPU is used)")
+            args.cpu_result = cpu_baseline_workload(args.workload, budget_s=args.cpu_budget)
     res = run_main(args) if args.workload == "main" else run_workload(args)
+    if args.workload != "main" and args.cpu_result is not None:
+        res["cpu_baseline"] = args.cpu_result
     if args.reference_copy_mb > 0:
         import torch
         n = args.reference_copy_mb << 20
