@@ -470,6 +470,7 @@ def run_decode_paged(args, g, dsa, gen, stream):
     gbps = nbytes / (t_p * 1e-3) / 1e9
     return {"metric": METRIC, "workload": "decode_128k_paged", "value": round(gbps, 1), "unit": "GB/s",
             "paged_us": round(t_p * 1e3, 2), "contiguous_us": round(t_c * 1e3, 2), "page_size": P,
+            "rows_per_s": round(B / (t_p * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
             "config": {"workload": "decode_128k_paged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
@@ -502,6 +503,7 @@ def run_decode_ragged(args, g, dsa, gen, stream):
     gbps = nbytes / (avg * 1e-3) / 1e9
     return {"metric": METRIC, "workload": "decode_128k_ragged", "value": round(gbps, 1), "unit": "GB/s",
             "us_per_call": round(avg * 1e3, 2), "tokens": int(sum(int(n) for n in lens)),
+            "rows_per_s": round(B / (avg * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
             "config": {"workload": "decode_128k_ragged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
@@ -540,6 +542,7 @@ def run_prefill_ragged(args, g, dsa, gen, stream):
     tf = flops / (t_r * 1e-3) / 1e12
     return {"metric": METRIC, "workload": "prefill_ragged", "value": round(tf, 2), "unit": "TFLOP/s",
             "ragged_ms": round(t_r, 4), "per_sequence_calls_ms": round(t_s, 4), "lengths": lens,
+            "rows_per_s": round(sum(lens) / (t_r * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
             "config": {"workload": "prefill_ragged", "sequences": len(lens), "total_rows": int(sum(lens)), "H": H,
@@ -568,7 +571,7 @@ def run_prefill_chunked(args, g, dsa, gen, stream):
     avg = sum(ms) / len(ms)
     tf = prefill_flops(L, H, D) / (avg * 1e-3) / 1e12
     return {"metric": METRIC, "workload": "prefill_32k_chunked", "value": round(tf, 2), "unit": "TFLOP/s",
-            "ms_per_sequence": round(avg, 4), "chunk_rows": C,
+            "ms_per_sequence": round(avg, 4), "chunk_rows": C, "rows_per_s": round(L / (avg * 1e-3), 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
             "config": {"workload": "prefill_32k_chunked", "L": L, "H": H, "D": D, "topk": topk, "chunk": C}}
