@@ -65,6 +65,35 @@ def test_paged_equals_contiguous_and_oracle(dsa, page, H, D):
                                 M=M[b]) is None, b
 
 
+def test_paged_lengths_outside_the_cache(dsa):
+    """Lengths of 0, below 0 and above the table's reach are clamped on the
+    device exactly as in the contiguous decode: empty rows of -1, and a
+    length past the last block reads every block."""
+    import torch
+    B, Lmax, D, H, topk, page = 4, 4096, 128, 64, 256, 64
+    rng = np.random.default_rng(31)
+    cache, ks = gen.quant_rows_e4m3(rng.standard_normal((B * Lmax, D)).astype(np.float32))
+    cache, ks = cache.reshape(B, Lmax, D), ks.reshape(B, Lmax)
+    q = gen.bf16_bits(rng.standard_normal((B, H, D)).astype(np.float32))
+    w = gen.bf16_bits((rng.standard_normal((B, H)) / 8).astype(np.float32))
+    lens = np.array([0, -5, Lmax + 904, 3000], dtype=np.int32)
+    dc, dk, dq, dw, dl = dev(cache), dev(ks), dev(q), dev(w), dev(lens)
+    note("decode paged lengths 0, negative and past the table")
+    idx_c, sc_c = dsa.dsa_indexer_topk_decode(dq, dw, dc, dk, dl, topk, want_scores=True)
+    pages, spages, table = _paginate(dc, dk, dl, page, seed=31)
+    idx_p, sc_p = dsa.dsa_indexer_topk_decode_paged(dq, dw, pages, spages, table, dl, topk, want_scores=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_p, idx_c) and torch.equal(sc_p, sc_c)
+    ih = host(idx_p)
+    assert np.all(ih[0] == -1) and np.all(ih[1] == -1)
+    res = oracle.decode(q, w, cache, ks, np.clip(lens, 0, Lmax), topk, return_scores=True)
+    M = parity.decode_query_mag(q, w, cache, ks, np.clip(lens, 0, Lmax))
+    sh = host(sc_p)
+    for b in (2, 3):
+        assert parity.check_row(ih[b], res["o"][b], res["A"][b], topk, g_score=sh[b], fmt="fp8q",
+                                M=M[b]) is None, b
+
+
 def test_paged_128k_batch_equals_contiguous(dsa):
     """B=32 x 131072 (the benchmark's decode), 64-token pages in shuffled order."""
     import torch
