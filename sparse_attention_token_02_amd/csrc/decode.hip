@@ -68,6 +68,8 @@ __device__ __forceinline__ int seq_len(const DecodeParams& p, int b) {
   return min(max(p.lens[b], 0), p.Lmax);   // lengths outside [0, Lmax] are clamped
 }
 
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
 // Buffer resource of `bytes` bytes at `base` (gfx9 descriptor word 3):
 // loads at offsets past `bytes` return 0 without touching memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
@@ -515,31 +517,12 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   if (lane == 0) wave_steps[wave] = nproc;
   __syncthreads();
 
-  // ---- tail.  The workgroup's histograms: words [0, HBINS/2) hold the fine
-  // bins in pairs, [HBINS/2, PW) the coarse bins (sums of FPC consecutive
-  // fine bins) in pairs.
+  // ---- tail.  Thread t holds fine bins 16t .. 16t + 15 (thread order = bin
+  // order), which are exactly coarse bin t.  The workgroup's histograms go
+  // out packed: words [0, HBINS/2) hold the fine bins in pairs, [HBINS/2, PW)
+  // the coarse bins in pairs.
+  static_assert(FPC == 16 && CBINS == DS_NT, "one coarse bin per thread");
   uint32_t* gh = p.hist + ((size_t)b * nwg + x) * PW;
-  for (int i = tid; i < HBINS / 8; i += DS_NT) {
-    const v4i lo = reinterpret_cast<const v4i*>(hist)[2 * i];
-    const v4i hi = reinterpret_cast<const v4i*>(hist)[2 * i + 1];
-    reinterpret_cast<v4i*>(gh)[i] = v4i{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16), hi[0] | (hi[1] << 16),
-                                        hi[2] | (hi[3] << 16)};
-  }
-  for (int i = tid; i < CBINS / 2; i += DS_NT) {
-    uint32_t c[2] = {0u, 0u};
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int q = 0; q < FPC / 4; ++q) {
-        const v4i t = reinterpret_cast<const v4i*>(hist)[(2 * i + h) * (FPC / 4) + q];
-        c[h] += (uint32_t)(t[0] + t[1] + t[2] + t[3]);
-      }
-    gh[HBINS / 2 + i] = c[0] | (c[1] << 16);
-  }
-  // Its min(k, n) best keys and the rest of their boundary bin.  Thread t
-  // holds bins 16t .. 16t + 15 (thread order = bin order); a suffix sum gives
-  // every bin the number of keys in higher bins, which becomes the bin's
-  // first output position.
   uint32_t h16[16], mine = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -550,6 +533,16 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
       mine += (uint32_t)t[j];
     }
   }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    reinterpret_cast<v4i*>(gh)[2 * tid + q] =
+        v4i{(int)(h16[8 * q] | (h16[8 * q + 1] << 16)), (int)(h16[8 * q + 2] | (h16[8 * q + 3] << 16)),
+            (int)(h16[8 * q + 4] | (h16[8 * q + 5] << 16)), (int)(h16[8 * q + 6] | (h16[8 * q + 7] << 16))};
+  const uint32_t next_coarse = (uint32_t)__shfl_down((int)mine, 1);
+  if ((tid & 1) == 0) gh[HBINS / 2 + tid / 2] = mine | (next_coarse << 16);
+  // Its min(k, n) best keys and the rest of their boundary bin: a suffix sum
+  // gives every bin the number of keys in higher bins, which becomes the
+  // bin's first output position.
   const int incl = wave_incl_sum((int)mine);
   int* wsum = reinterpret_cast<int*>(ktr);     // the transpose area is free now
   if (lane == 63) wsum[wave] = incl;
@@ -557,7 +550,7 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
     sh_cut[0] = HBINS;
     sh_cut[1] = 0;
   }
-  __syncthreads();                             // also: every thread has read its counts
+  __syncthreads();
   int higher_waves = 0, total = 0;
 #pragma unroll
   for (int w2 = 0; w2 < DS_WAVES; ++w2) {
@@ -568,47 +561,66 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   const int wave_tot = __builtin_amdgcn_readlane(incl, 63);
   uint32_t above = (uint32_t)(higher_waves + wave_tot - incl);   // keys in bins above this thread's
   const uint32_t kk_w = (uint32_t)min(p.topk, total);
+  uint32_t first[16];
 #pragma unroll
   for (int j = 15; j >= 0; --j) {
-    const int bin = 16 * tid + j;
     if (above < kk_w && above + h16[j] >= kk_w) {
-      sh_cut[0] = bin;
+      sh_cut[0] = 16 * tid + j;
       sh_cut[1] = (int)(above + h16[j]);   // keys at or above the boundary bin
     }
-    hist[bin] = above;                      // output position of the bin's first key
+    first[j] = above;                       // output position of the bin's first key
     above += h16[j];
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    reinterpret_cast<v4i*>(hist)[4 * tid + q] =
+        v4i{(int)first[4 * q], (int)first[4 * q + 1], (int)first[4 * q + 2], (int)first[4 * q + 3]};
   __syncthreads();
   const uint32_t dcut = (uint32_t)sh_cut[0];
-  uint2* cand = p.cand + ((size_t)b * nwg + x) * DS_KCAP;
-  // eight keys per thread at a time, so that the LDS reads, the position
-  // atomics and the stores of a batch overlap
-  constexpr int SCAT = 8;
+  // the workgroup's list: positions below DS_KCAP (positions count kept keys)
+  const __amdgpu_buffer_rsrc_t crs = buf_rsrc(p.cand + ((size_t)b * nwg + x) * DS_KCAP, DS_KCAP * 8u);
+  uint32_t* dummy = reinterpret_cast<uint32_t*>(ktr) + 64;   // per thread, past wsum
   int nslot = 0;                         // stage slots in use: the longest wave's steps
 #pragma unroll
   for (int w2 = 0; w2 < DS_WAVES; ++w2) nslot = max(nslot, wave_steps[w2]);
   nslot *= 32 * DS_WAVES;
+  // Eight slots per thread per pass, as two runs of four consecutive slots.
+  // Stage slot e is key e % 32 of step e / 128 of wave (e / 32) % 4, so a run
+  // lies in one 32-key step: one chunk lookup and one 16-byte read per run.
+  // nslot is a multiple of 128 and at most DS_KCAP, a whole number of
+  // passes, so every read stays in the stage; runs past nslot are masked.
+  constexpr int SCAT = 8;
+  static_assert(DS_KCAP % (SCAT * DS_NT) == 0, "whole passes over the stage");
+  const uint32_t* stage = reinterpret_cast<const uint32_t*>(sc_stage);
   for (int e0 = 0; e0 < nslot; e0 += SCAT * DS_NT) {
     uint32_t key[SCAT];
     int sidx[SCAT];
 #pragma unroll
-    for (int u = 0; u < SCAT; ++u) {
-      // stage slot: step e / 128, wave (e / 32) % 4, key e % 32 (slots past
-      // nslot are masked; the reads stay in bounds)
-      const int e = min(e0 + u * DS_NT + tid, DS_KCAP - 1);
-      const int cr = step_chunk[(e >> 5) % DS_WAVES][e / (32 * DS_WAVES)];   // read unconditionally: no branch
-      const int c = e0 + u * DS_NT + tid < nslot ? cr : -1;
+    for (int h = 0; h < 2; ++h) {
+      const int e = e0 + h * (4 * DS_NT) + 4 * tid;
+      const v4i kv = *reinterpret_cast<const v4i*>(stage + e);
+      const int cr = step_chunk[(e >> 5) % DS_WAVES][e / (32 * DS_WAVES)];
+      const int c = e < nslot ? cr : -1;
       const int s = 32 * c + (e & 31);
-      sidx[u] = (c >= 0 && s < len) ? s : -1;
-      key[u] = reinterpret_cast<const uint32_t*>(sc_stage)[e];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        key[4 * h + j] = (uint32_t)kv[j];
+        sidx[4 * h + j] = (c >= 0 && s + j < len) ? s + j : -1;
+      }
     }
+    // Without branches: a key that is not kept adds 0 to this thread's own
+    // dummy word, and its store goes to the first byte past the list's
+    // record limit, where the buffer store writes nothing.
     uint32_t pos[SCAT];
 #pragma unroll
-    for (int u = 0; u < SCAT; ++u)
-      if (sidx[u] >= 0 && (key[u] >> 20) >= dcut) pos[u] = atomicAdd(&hist[key[u] >> 20], 1u);
+    for (int u = 0; u < SCAT; ++u) {
+      const bool kept = sidx[u] >= 0 && (key[u] >> 20) >= dcut;
+      pos[u] = atomicAdd(kept ? &hist[key[u] >> 20] : &dummy[tid], kept ? 1u : 0u);
+      pos[u] = kept ? pos[u] * 8u : DS_KCAP * 8u;
+    }
 #pragma unroll
     for (int u = 0; u < SCAT; ++u)
-      if (sidx[u] >= 0 && (key[u] >> 20) >= dcut) cand[pos[u]] = make_uint2(key[u], (uint32_t)sidx[u]);
+      __builtin_amdgcn_raw_buffer_store_b64(v2u{key[u], (uint32_t)sidx[u]}, crs, (int)pos[u], 0, 0);
   }
   if (tid == 0) p.wgcut[(size_t)b * nwg + x] = make_int2(sh_cut[0], sh_cut[1]);
 }
