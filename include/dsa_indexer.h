@@ -90,10 +90,9 @@ dsa_status dsa_indexer_topk_prefill_workspace(int L, int H, int D, int topk, dsa
  * k        [L, D] dt             keys, one vector per token shared by all heads
  * k_scale  [L] fp32 or NULL (= 1)
  * w        [L, H] bf16           head weights
- * L >= 1; H a multiple of 8 with 8 <= H <= 64 (kernels are built for H in
- * {8, 16, 32, 64}; other counts run on the next of these with zero heads
- * appended); D in {64, 128}; bf16 with D=128 needs H <= 32;
- * 1 <= topk <= 4096.
+ * L >= 1; H a multiple of 8 with 8 <= H <= 128 (kernels are built for H in
+ * {8, 16, 32, 64, 128}; other counts run on the next of these with zero
+ * heads appended); D in {64, 128}; 1 <= topk <= 4096.
  * out_idx        [L, topk] int32  selected keys, ascending, -1 padded (written in full).
  *                A key whose score is NaN or -inf (finite but extreme inputs can
  *                overflow) is never selected; its row then holds fewer than
@@ -184,8 +183,8 @@ dsa_status dsa_indexer_topk_decode_workspace(int B, int Lmax, int H, int D, int 
  *                                not checked: a value outside [0, Lmax] is clamped
  *                                into it, and a length of 0 gives a row of -1 with
  *                                -inf scores)
- * B >= 1; H a multiple of 8 with 8 <= H <= 64 (run on the kernel built for
- * the next of {16, 32, 64}, zero heads appended); D in {64, 128};
+ * B >= 1; H a multiple of 8 with 8 <= H <= 128 (run on the kernel built for
+ * the next of {16, 32, 64, 128}, zero heads appended); D in {64, 128};
  * 1 <= Lmax <= 262144; 1 <= topk <= 4096.
  * out_idx        [B, topk] int32 ascending, -1 padded
  * out_topk_score [B, topk] fp32 or NULL

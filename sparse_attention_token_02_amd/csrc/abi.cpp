@@ -86,17 +86,18 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int prefill_cap(int dt, int H, int D, int topk) { return dsa::prefill_list_capacity(dt, H, D, topk); }
 
-int prefill_slots(int L, int H) {
-  const int rw = dsa::prefill_rows_per_item(H);
+int prefill_slots(int L, int dt, int H, int D) {
+  const int rw = dsa::prefill_rows_per_item(dt, H, D);
   const int items = (L + rw - 1) / rw;
   return items < kMaxSlots ? items : kMaxSlots;
 }
 
 size_t prefill_ws_bytes(int L, int H, int D, int topk, dsa_dtype dt) {
-  const size_t per = (size_t)dsa::prefill_rows_per_item(H) * prefill_cap((int)dt, H, D, topk);
-  const size_t lists = align_up((size_t)prefill_slots(L, H) * per * 4, 256);
-  DSA_DCHECK(per > 0 && prefill_slots(L, H) >= 1 && prefill_slots(L, H) <= kMaxSlots);
-  DSA_DCHECK(kHeader % 256 == 0 && lists >= (size_t)prefill_slots(L, H) * per * 4);
+  const int slots = prefill_slots(L, (int)dt, H, D);
+  const size_t per = (size_t)dsa::prefill_rows_per_item((int)dt, H, D) * prefill_cap((int)dt, H, D, topk);
+  const size_t lists = align_up((size_t)slots * per * 4, 256);
+  DSA_DCHECK(per > 0 && slots >= 1 && slots <= kMaxSlots);
+  DSA_DCHECK(kHeader % 256 == 0 && lists >= (size_t)slots * per * 4);
   return kHeader + 2 * lists;
 }
 
@@ -175,9 +176,9 @@ dsa_status launch_prefill(const PrefillArgs& a) {
   p.out_idx = a.out_idx;
   p.out_score = a.out_score;
   p.out_dense = a.out_dense;
-  const int rw = dsa::prefill_rows_per_item(a.H);
+  const int rw = dsa::prefill_rows_per_item((int)a.dt, a.H, a.D);
   p.n_items = (a.L + rw - 1) / rw;
-  const int slots = prefill_slots(a.L, a.H);
+  const int slots = prefill_slots(a.L, (int)a.dt, a.H, a.D);
   uint8_t* base = static_cast<uint8_t*>(a.ws);
   p.counter = reinterpret_cast<int*>(base);
   const size_t lst = align_up((size_t)slots * rw * p.cap * 4, 256);
@@ -364,7 +365,7 @@ struct VarlenWs {
 };
 
 static bool varlen_ws(int nseq, int total_q, int H, int D, int topk, dsa_dtype dt, VarlenWs* w) {
-  const int rw = dsa::prefill_rows_per_item(H);
+  const int rw = dsa::prefill_rows_per_item((int)dt, H, D);
   const int64_t cap = ((int64_t)total_q + rw - 1) / rw + nseq;
   if (cap > INT32_MAX / 2) return false;
   w->cap_items = (int)cap;
@@ -415,7 +416,7 @@ dsa_status dsa_indexer_topk_prefill_varlen(const void* q, const float* q_scale, 
   VarlenWs lay;
   varlen_ws(nseq, total_q, H, D, topk, dt, &lay);
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  const int rw = dsa::prefill_rows_per_item(H);
+  const int rw = dsa::prefill_rows_per_item((int)dt, H, D);
   dsa::PrefillParams p{};
   p.q = static_cast<const uint8_t*>(q);
   p.q_scale = q_scale;

@@ -124,8 +124,10 @@ __device__ __forceinline__ int limb_exp(float m) {
 
 }  // namespace
 
+// Two workgroups per CU, except at H = 128, whose query limbs alone take
+// 128 registers: one wave per SIMD.
 template <int H, int D, bool PAGED>
-__global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(DS_NT, H > 64 ? 1 : 2) decode_score_kernel(DecodeParams p) {
   constexpr int MB = (H + 31) / 32;
   constexpr int KS = D / 64;              // fp8 MFMA steps along D
   constexpr int NK = 2 * KS;              // with the two limbs of q stacked along K
@@ -240,16 +242,20 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // {h HALF + 32 ks + 16 c + i : h < 2, i < 16}, which MFMA step ks reads
   // from bytes [16c, 16c + 16) of both lane halves; thread blk owns block blk.
   constexpr int NBLK = 32 * MB * KS * 2;
-  static_assert(NBLK <= DS_NT, "one query block per thread");
-  const int qhead = tid / (KS * 2), qks = (tid >> 1) % KS, qc = tid & 1;
-  v4i qraw[2][2];
+  constexpr int QB = (NBLK + DS_NT - 1) / DS_NT;   // query blocks per thread: block tid + DS_NT j
+  v4i qraw[QB][2][2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    qraw[h][0] = qraw[h][1] = v4i{0, 0, 0, 0};
-    if (tid < NBLK && qhead < p.hr) {
-      const uint16_t* src = p.q + ((size_t)b * p.hr + qhead) * D + h * HALF + 32 * qks + 16 * qc;
-      qraw[h][0] = *reinterpret_cast<const v4i*>(src);
-      qraw[h][1] = *reinterpret_cast<const v4i*>(src + 8);
+  for (int j = 0; j < QB; ++j) {
+    const int blk = tid + DS_NT * j;
+    const int qhead = blk / (KS * 2), qks = (blk >> 1) % KS, qc = blk & 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      qraw[j][h][0] = qraw[j][h][1] = v4i{0, 0, 0, 0};
+      if (blk < NBLK && qhead < p.hr) {
+        const uint16_t* src = p.q + ((size_t)b * p.hr + qhead) * D + h * HALF + 32 * qks + 16 * qc;
+        qraw[j][h][0] = *reinterpret_cast<const v4i*>(src);
+        qraw[j][h][1] = *reinterpret_cast<const v4i*>(src + 8);
+      }
     }
   }
   // head weights: result register j of block mb in this lane is head
@@ -371,18 +377,25 @@ __global__ void __launch_bounds__(DS_NT, 2) decode_score_kernel(DecodeParams p) 
   // way (a bf16 value has 8 significant bits, a limb 4).  Staged in operand
   // order, [mb][kk][c][lane][16 bytes] with kk = limb * KS + ks, and one
   // scale word per (mb, lane): byte kk for lane (row, c).
-  uint8_t* lstage = &ktr[0][0];
-  int* lscale = reinterpret_cast<int*>(sc_stage);
-  static_assert(MB * NK * 2 * 64 * 16 <= (int)sizeof(ktr) && MB * 64 * 4 <= (int)sizeof(sc_stage), "limb staging");
-  if (tid < NBLK) {
-    const int ks = qks, c = qc;
+  // (at H = 128 the limbs outgrow the transpose buffer: they take the
+  // score stage, and their scales the transpose buffer)
+  constexpr bool QBIG = MB * NK * 2 * 64 * 16 > (int)sizeof(ktr);
+  uint8_t* lstage = QBIG ? reinterpret_cast<uint8_t*>(sc_stage) : &ktr[0][0];
+  int* lscale = QBIG ? reinterpret_cast<int*>(&ktr[0][0]) : reinterpret_cast<int*>(sc_stage);
+  static_assert(MB * NK * 2 * 64 * 16 <= (int)(QBIG ? sizeof(sc_stage) : sizeof(ktr)) &&
+                MB * 64 * 4 <= (int)(QBIG ? sizeof(ktr) : sizeof(sc_stage)), "limb staging");
+#pragma unroll
+  for (int jb = 0; jb < QB; ++jb) {
+    const int blk = tid + DS_NT * jb;
+    if (blk >= NBLK) break;
+    const int qhead = blk / (KS * 2), ks = (blk >> 1) % KS, c = blk & 1;
     const int mb = qhead >> 5, row = qhead & 31;
     float v[32];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const uint32_t wd = (uint32_t)qraw[h][i >> 3][(i & 7) >> 1];
+        const uint32_t wd = (uint32_t)qraw[jb][h][i >> 3][(i & 7) >> 1];
         v[16 * h + i] = __uint_as_float((i & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
       }
 #pragma unroll
@@ -1003,6 +1016,7 @@ DecodeWsSizes decode_ws_sizes(int Lmax) {
 
 template <int H, int D>
 static void launch_score(const DecodeParams& p, hipStream_t stream) {
+  static_assert(H <= 128, "head width");
   dim3 grid(score_workgroups(p.Lmax) * p.B);
   if (p.block_table) hipLaunchKernelGGL((decode_score_kernel<H, D, true>), grid, dim3(DS_NT), 0, stream, p);
   else hipLaunchKernelGGL((decode_score_kernel<H, D, false>), grid, dim3(DS_NT), 0, stream, p);
@@ -1010,7 +1024,9 @@ static void launch_score(const DecodeParams& p, hipStream_t stream) {
 
 hipError_t decode_launch(const DecodeParams& p, int H, int D, hipStream_t stream) {
   H = decode_head_width(H);
-  if (H == 64 && D == 128) launch_score<64, 128>(p, stream);
+  if (H == 128 && D == 128) launch_score<128, 128>(p, stream);
+  else if (H == 128 && D == 64) launch_score<128, 64>(p, stream);
+  else if (H == 64 && D == 128) launch_score<64, 128>(p, stream);
   else if (H == 64 && D == 64) launch_score<64, 64>(p, stream);
   else if (H == 32 && D == 128) launch_score<32, 128>(p, stream);
   else if (H == 32 && D == 64) launch_score<32, 64>(p, stream);

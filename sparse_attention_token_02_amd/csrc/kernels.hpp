@@ -49,16 +49,16 @@ hipError_t prefill_varlen_prepare(const int32_t* cu_q, const int32_t* cu_k, int 
 
 constexpr int MAX_TOPK = 4096;   // the largest k the library accepts
 
-// Head counts: any multiple of 8 up to 64 runs on the kernels built for the
-// next width in {8, 16, 32, 64} (decode: {16, 32, 64}), the extra heads
-// zero (their dot products, weights and scores contribute nothing).
+// Head counts: any multiple of 8 up to 128 runs on the kernels built for the
+// next width in {8, 16, 32, 64, 128} (decode: {16, 32, 64, 128}), the extra
+// heads zero (their dot products, weights and scores contribute nothing).
 inline int prefill_head_width(int H) {
-  if (H < 8 || H > 64 || H % 8) return 0;
-  return H <= 8 ? 8 : H <= 16 ? 16 : H <= 32 ? 32 : 64;
+  if (H < 8 || H > 128 || H % 8) return 0;
+  return H <= 8 ? 8 : H <= 16 ? 16 : H <= 32 ? 32 : H <= 64 ? 64 : 128;
 }
 inline int decode_head_width(int H) {
-  if (H < 8 || H > 64 || H % 8) return 0;
-  return H <= 16 ? 16 : H <= 32 ? 32 : 64;
+  if (H < 8 || H > 128 || H % 8) return 0;
+  return H <= 16 ? 16 : H <= 32 ? 32 : H <= 64 ? 64 : 128;
 }
 
 // Per-sequence header of the decode workspace: the pool claim counter
@@ -139,7 +139,7 @@ struct OverlapParams {
 
 // prefill.hip
 bool prefill_supported(int dt, int H, int D);
-int prefill_rows_per_item(int H);
+int prefill_rows_per_item(int dt, int H, int D);
 int prefill_list_capacity(int dt, int H, int D, int topk);
 int prefill_sample_keys(int dt, int H, int D);
 hipError_t prefill_launch(const PrefillParams& p, int dt, int H, int D, int grid, hipStream_t stream);

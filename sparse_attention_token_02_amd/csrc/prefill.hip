@@ -7,7 +7,9 @@
 // and, per query row t, the min(k, t+1) best keys under "score descending,
 // key index ascending", written in ascending key order and padded with -1.
 //
-// Design (one work item = RW consecutive query rows, 8 waves):
+// Design (one work item = RW consecutive query rows, 8 waves; 4 waves, one
+// per SIMD, for the configurations whose registers do not fit two waves per
+// SIMD: H = 128, and bf16 at H = 64 with D = 128):
 // * Score contraction on MFMA.  Index heads sit on the MFMA row dimension and
 //   keys on the column dimension.  With the 32x32 accumulator layout a lane
 //   owns one key column and 16 rows of each 32-row block.
@@ -59,12 +61,15 @@ namespace dsa {
 
 namespace {
 
-constexpr int NT = 512;      // threads per workgroup (8 waves)
-constexpr int WAVES = NT / 64;
-
 template <int DT, int H, int D>
 struct PfCfg {
   static constexpr bool FP8 = (DT == DSA_FP8_E4M3);
+  // one wave per SIMD where a wave's registers exceed half the SIMD's file:
+  // the query operands, head weights and accumulators of 128 heads, or the
+  // eight 16-deep bf16 K steps (operands and B ring) of a 128-wide row
+  static constexpr bool WIDE = H == 128 || (!FP8 && H == 64 && D == 128);
+  static constexpr int NT = WIDE ? 256 : 512;       // threads per workgroup
+  static constexpr int WAVES = NT / 64;
   // H >= 32: one query per wave; each 32-row MFMA block holds 32 of its heads,
   // so the two lane halves hold different heads of the same query and one
   // cross-half add finishes the head sum.  H <= 16: each lane half holds its
@@ -91,7 +96,7 @@ struct PfCfg {
   static constexpr int RPB = 256 / ROWB;            // key rows per 256-byte bank sweep
   static constexpr int NLD = TK * ROWB / 1024;      // 1 KB direct-to-LDS loads per tile
   static_assert(ROWB <= 256 && NLD % WAVES == 0, "tile layout");
-  static_assert(H == 8 || H == 16 || H == 32 || H == 64, "unsupported head count");
+  static_assert(H == 8 || H == 16 || H == 32 || H == 64 || H == 128, "unsupported head count");
   static_assert(D % KM == 0 && ROWB / 2 == KS * SB, "unsupported head dim");
   static_assert(RW <= 32, "row mask is 32 bits");
   // query slot of accumulator register j (result row 8(j/4) + 4*half + j%4)
@@ -105,7 +110,7 @@ template <int DT, int H, int D>
 struct PfShared {
   using C = PfCfg<DT, H, D>;
   __attribute__((aligned(16))) float kscale[2][C::TK];
-  uint32_t whist[WAVES][256];              // per-wave radix histogram (selection, sample quantile)
+  uint32_t whist[C::WAVES][256];           // per-wave radix histogram (selection, sample quantile)
   __attribute__((aligned(16))) float weff[C::RW * H];   // folded head weights w*q_scale of the item's rows
   int row_cnt[C::RW];
   int item;
@@ -157,8 +162,10 @@ __device__ __forceinline__ v16f mma(typename Opnd<FP8>::T a, typename Opnd<FP8>:
 }  // namespace
 
 template <int DT, int H, int D, bool DENSE>
-__global__ void __launch_bounds__(NT, 1) prefill_kernel(PrefillParams p) {
+__global__ void __launch_bounds__((PfCfg<DT, H, D>::NT), 1) prefill_kernel(PrefillParams p) {
   using C = PfCfg<DT, H, D>;
+  constexpr int NT = C::NT;
+  constexpr int WAVES = C::WAVES;
   using OT = typename Opnd<C::FP8>::T;
   __shared__ PfShared<DT, H, D> sh;
   // dynamic LDS: the sampled scores of every row (RW rows x sample_m floats)
@@ -781,7 +788,7 @@ static hipError_t launch_variant(const PrefillParams& p, int grid, hipStream_t s
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<DT, H, D, DENSE>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_kernel<DT, H, D, DENSE>), dim3(grid), dim3(NT), dyn, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<DT, H, D, DENSE>), dim3(grid), dim3(PfCfg<DT, H, D>::NT), dyn, stream, p);
   return hipGetLastError();
 }
 
@@ -796,17 +803,19 @@ static hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t strea
   X(DSA_FP8_E4M3, 32, 64) X(DSA_FP8_E4M3, 16, 128) X(DSA_FP8_E4M3, 16, 64)         \
   X(DSA_FP8_E4M3, 8, 128) X(DSA_FP8_E4M3, 8, 64) X(DSA_BF16, 64, 64)               \
   X(DSA_BF16, 32, 128) X(DSA_BF16, 32, 64) X(DSA_BF16, 16, 128) X(DSA_BF16, 16, 64) \
-  X(DSA_BF16, 8, 128) X(DSA_BF16, 8, 64)
+  X(DSA_BF16, 8, 128) X(DSA_BF16, 8, 64) X(DSA_BF16, 64, 128) X(DSA_FP8_E4M3, 128, 128)    \
+  X(DSA_FP8_E4M3, 128, 64) X(DSA_BF16, 128, 128) X(DSA_BF16, 128, 64)
 
 struct PfInfo {
   size_t static_lds;   // bytes of the kernel's static shared memory
   int tile_keys;       // keys per LDS tile
+  int rows;            // query rows per work item
 };
 
 static bool pf_info(int dt, int H, int D, PfInfo* out) {
 #define DSA_PF_INFO(DT_, H_, D_)                                                 \
   if (dt == DT_ && H == H_ && D == D_) {                                         \
-    *out = PfInfo{sizeof(PfShared<DT_, H_, D_>), PfCfg<DT_, H_, D_>::TK};          \
+    *out = PfInfo{sizeof(PfShared<DT_, H_, D_>), PfCfg<DT_, H_, D_>::TK, PfCfg<DT_, H_, D_>::RW};  \
     return true;                                                                 \
   }
   DSA_PF_CONFIGS(DSA_PF_INFO)
@@ -814,9 +823,9 @@ static bool pf_info(int dt, int H, int D, PfInfo* out) {
   return false;
 }
 
-int prefill_rows_per_item(int H) {
-  H = prefill_head_width(H);
-  return H >= 32 ? WAVES : WAVES * 2 * (16 / H);
+int prefill_rows_per_item(int dt, int H, int D) {
+  PfInfo info;
+  return pf_info(dt, prefill_head_width(H), D, &info) ? info.rows : 0;
 }
 
 bool prefill_supported(int dt, int H, int D) {
@@ -833,7 +842,7 @@ int prefill_sample_keys(int dt, int H, int D) {
   if (!pf_info(dt, prefill_head_width(H), D, &info)) return 0;
   const size_t lds_limit = 160 * 1024;
   const int tk = info.tile_keys;
-  const int rw = prefill_rows_per_item(H);
+  const int rw = info.rows;
   if (info.static_lds >= lds_limit) return 0;
   int m = (int)((lds_limit - info.static_lds) / ((size_t)rw * sizeof(float)));
   m = m / tk * tk;

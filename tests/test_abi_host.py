@@ -75,11 +75,10 @@ def test_prefill_workspace_query():
                      ((1024, 64, 128, 0, "fp8"), dsa.DSA_ERR_INVALID_ARG),
                      ((1024, 64, 128, 5000, "fp8"), dsa.DSA_ERR_INVALID_ARG),
                      ((1024, 44, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
-                     ((1024, 72, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
-                     ((1024, 48, 128, 64, "bf16"), dsa.DSA_ERR_UNSUPPORTED),
+                     ((1024, 136, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
+                     ((1024, 48, 32, 64, "bf16"), dsa.DSA_ERR_UNSUPPORTED),
                      ((1024, 64, 96, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
-                     ((1024, 128, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED),
-                     ((1024, 64, 128, 64, "bf16"), dsa.DSA_ERR_UNSUPPORTED)]:
+                     ((1024, 256, 128, 64, "fp8"), dsa.DSA_ERR_UNSUPPORTED)]:
         with pytest.raises(dsa.DsaError) as e:
             dsa.dsa_indexer_topk_prefill_workspace(*args)
         assert e.value.status == st, args
@@ -88,6 +87,11 @@ def test_prefill_workspace_query():
         dsa.dsa_indexer_topk_prefill_workspace(1024, 64, 128, 64, "fp8")
     assert dsa.dsa_indexer_topk_prefill_workspace(1024, 24, 64, 64, "bf16") == \
         dsa.dsa_indexer_topk_prefill_workspace(1024, 32, 64, 64, "bf16")
+    assert dsa.dsa_indexer_topk_prefill_workspace(1024, 72, 128, 64, "fp8") == \
+        dsa.dsa_indexer_topk_prefill_workspace(1024, 128, 128, 64, "fp8")
+    # the one-wave-per-SIMD configurations are built too
+    for H, D, dt in [(128, 128, "fp8"), (128, 64, "fp8"), (128, 128, "bf16"), (128, 64, "bf16"), (64, 128, "bf16")]:
+        assert dsa.dsa_indexer_topk_prefill_workspace(1024, H, D, 64, dt) > 0
     lib = dsa.lib()
     assert lib.dsa_indexer_topk_prefill_workspace(16, 8, 64, 4, 7, ctypes.byref(ctypes.c_size_t())) == \
         dsa.DSA_ERR_INVALID_ARG
@@ -166,8 +170,7 @@ def test_decode_rejects_before_any_device_call():
     assert call(lens=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(B=0) == dsa.DSA_ERR_INVALID_ARG
     assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
-    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
-    assert call(H=128) == dsa.DSA_ERR_UNSUPPORTED             # out on purpose: the register budget
+    assert call(H=136) == dsa.DSA_ERR_UNSUPPORTED
     assert call(Lmax=1 << 20) == dsa.DSA_ERR_UNSUPPORTED
     assert call(wsb=100) == dsa.DSA_ERR_WORKSPACE
     assert call(c=FAKE + 8) == dsa.DSA_ERR_INVALID_ARG
@@ -185,7 +188,7 @@ def test_decode_paged_rejects_before_any_device_call():
     assert call(table=None) == dsa.DSA_ERR_INVALID_ARG
     assert call(mb=8193) == dsa.DSA_ERR_UNSUPPORTED          # more than 262144 tokens
     assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
-    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=136) == dsa.DSA_ERR_UNSUPPORTED
     assert call(wsb=64) == dsa.DSA_ERR_WORKSPACE
     assert call(c=FAKE + 4) == dsa.DSA_ERR_INVALID_ARG
 
@@ -244,7 +247,7 @@ def test_run_decode_layers_rejects_before_any_device_call():
     assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
     assert "layer 0" in dsa.dsa_last_error()
     assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
-    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=136) == dsa.DSA_ERR_UNSUPPORTED
     assert call(qq=arr(FAKE, FAKE, None)) == dsa.DSA_ERR_INVALID_ARG     # layer 2 is F and has no q
     assert "layer 2" in dsa.dsa_last_error()
     assert call(cache=arr(FAKE, FAKE, FAKE + 8)) == dsa.DSA_ERR_INVALID_ARG   # misaligned cache of layer 2
@@ -275,7 +278,7 @@ def test_run_decode_layers_mli_rejects_before_any_device_call():
     assert call(wsb=16) == dsa.DSA_ERR_WORKSPACE
     assert "layer 0" in dsa.dsa_last_error()
     assert call(H=12) == dsa.DSA_ERR_UNSUPPORTED
-    assert call(H=72) == dsa.DSA_ERR_UNSUPPORTED
+    assert call(H=136) == dsa.DSA_ERR_UNSUPPORTED
     assert call(qq=P(FAKE, FAKE, None)) == dsa.DSA_ERR_INVALID_ARG
     assert "layer 2" in dsa.dsa_last_error()
 

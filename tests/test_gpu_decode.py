@@ -45,7 +45,8 @@ def _compare(idx, sc, inp, topk, seqs=None):
         assert err is None, (b, err)
 
 
-@pytest.mark.parametrize("H,D", [(64, 128), (32, 64), (16, 128), (8, 64), (40, 128), (56, 64)])
+@pytest.mark.parametrize("H,D", [(64, 128), (32, 64), (16, 128), (8, 64), (40, 128), (56, 64), (128, 128),
+                                 (128, 64), (96, 128)])
 def test_decode_small_every_sequence(dsa, H, D):
     lens = [5000, 4097, 256, 100, 1, 2049]
     inp = _small_inputs(6, 5000, H, D, lens, seed=H + D)

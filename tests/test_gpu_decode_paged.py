@@ -40,7 +40,7 @@ def _paginate(cache, k_scale, lens, page, seed, spare=3):
 
 
 @pytest.mark.parametrize("page,H,D", [(32, 64, 128), (64, 64, 128), (256, 64, 128), (64, 16, 64), (128, 32, 128),
-                                      (32, 64, 64)])
+                                      (32, 64, 64), (64, 128, 128)])
 def test_paged_equals_contiguous_and_oracle(dsa, page, H, D):
     import torch
     B, Lmax, topk = 5, 4096, 256

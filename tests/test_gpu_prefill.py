@@ -176,7 +176,9 @@ def test_prefill_32k_full_size_sampled_rows(dsa):
 # sizes.  Ragged L (not a multiple of the 8- to 32-row work item or of a tile).
 BUILT = [("fp8", 64, 128), ("fp8", 64, 64), ("fp8", 32, 128), ("fp8", 32, 64), ("fp8", 16, 128),
          ("fp8", 16, 64), ("fp8", 8, 128), ("fp8", 8, 64), ("bf16", 64, 64), ("bf16", 32, 128),
-         ("bf16", 32, 64), ("bf16", 16, 128), ("bf16", 16, 64), ("bf16", 8, 128), ("bf16", 8, 64)]
+         ("bf16", 32, 64), ("bf16", 16, 128), ("bf16", 16, 64), ("bf16", 8, 128), ("bf16", 8, 64),
+         # one wave per SIMD (4 rows per work item)
+         ("fp8", 128, 128), ("fp8", 128, 64), ("bf16", 128, 128), ("bf16", 128, 64), ("bf16", 64, 128)]
 
 
 @pytest.mark.parametrize("dt,H,D", BUILT)
@@ -193,7 +195,7 @@ def test_every_built_configuration(dsa, dt, H, D):
 
 
 @pytest.mark.parametrize("dt,H,D", [("fp8", 24, 128), ("fp8", 40, 64), ("fp8", 56, 128), ("bf16", 24, 64),
-                                     ("bf16", 48, 64)])
+                                     ("bf16", 48, 64), ("fp8", 96, 128), ("bf16", 72, 64)])
 def test_head_counts_between_the_built_widths(dsa, dt, H, D):
     """H a multiple of 8 that no kernel is built for runs on the next
     built width with zero heads appended; the caller's [L, H, D] layout is

@@ -176,7 +176,8 @@ def test_varlen_many_short_sequences_against_oracle(dsa):
             assert parity.check_row(ih[g], res["o"][j], res["A"][j], topk, g_score=sh[g]) is None, (i, j)
 
 
-@pytest.mark.parametrize("dt,H,D", [("bf16", 16, 64), ("fp8", 8, 128), ("bf16", 32, 128)])
+@pytest.mark.parametrize("dt,H,D", [("bf16", 16, 64), ("fp8", 8, 128), ("bf16", 32, 128), ("fp8", 128, 128),
+                                     ("bf16", 64, 128)])
 def test_varlen_other_shapes_equal_per_sequence_calls(dsa, dt, H, D):
     """The ragged batch for other built (dtype, H, D): per-head scales for fp8,
     none for bf16; every sequence equals its own chunk call."""
