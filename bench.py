@@ -11,8 +11,9 @@ holds only the two library calls.
 Prints one JSON line.  ``value`` is the prefill throughput in algorithmic
 TFLOP/s (2*H*D multiply-adds per causal (query, key) pair); the decode rate
 in algorithmic GB/s is reported beside it.  Other workloads
-(``--workload tiny|prefill_196k|prefill_32k_chunked|prefill_ragged|decode_128k_paged|
-decode_128k_ragged|fs_47|fs_decode_47|mli_decode_47``)
+(``--workload tiny|prefill_196k|prefill_32k_chunked|prefill_ragged|prefill_32k_h128|
+prefill_32k_bf16|decode_128k_paged|decode_128k_ragged|decode_128k_h128|fs_47|fs_decode_47|
+mli_decode_47``)
 print their own line.
 """
 from __future__ import annotations
@@ -406,8 +407,8 @@ def run_workload(args):
     g = DeviceGen(dev)
     stream = torch.cuda.current_stream(dev)
     name = args.workload
-    if name in ("tiny", "prefill_196k", "prefill_32k"):
-        cfg = gen.CONFIGS[name]
+    if name in ("tiny", "prefill_196k", "prefill_32k", "prefill_32k_h128", "prefill_32k_bf16"):
+        cfg = shape_config(gen, name)
         L, H, D, topk = cfg["L"], cfg["H"], cfg["D"], cfg["topk"]
         p = g.prefill_inputs(cfg)
         out = torch.empty((L, topk), dtype=torch.int32, device=dev)
@@ -430,6 +431,8 @@ def run_workload(args):
         return run_decode_paged(args, g, dsa, gen, stream)
     if name == "decode_128k_ragged":
         return run_decode_ragged(args, g, dsa, gen, stream)
+    if name == "decode_128k_h128":
+        return run_decode_ragged(args, g, dsa, gen, stream, cfg=shape_config(gen, name), name=name)
     if name == "prefill_32k_chunked":
         return run_prefill_chunked(args, g, dsa, gen, stream)
     if name == "fs_47":
@@ -481,12 +484,28 @@ def run_decode_paged(args, g, dsa, gen, stream):
                        "page_size": P}}
 
 
-def run_decode_ragged(args, g, dsa, gen, stream):
+def shape_config(gen, name):
+    """The recipe of a named workload; the _h128 and _bf16 variants are the
+    32K prefill and the 128K decode at 128 index heads (head weights scaled
+    by 1/sqrt(128)), and the 32K prefill with bf16 queries and keys."""
+    import math
+    import numpy as np
+    w128 = float(np.float32(math.sqrt(128.0)))
+    if name == "prefill_32k_h128":
+        return dict(gen.CONFIGS["prefill_32k"], H=128, w_div=w128)
+    if name == "prefill_32k_bf16":
+        return dict(gen.CONFIGS["prefill_32k"], dtype="bf16", qk_div=8.0)
+    if name == "decode_128k_h128":
+        return dict(gen.CONFIGS["decode_128k"], H=128, w_div=w128)
+    return gen.CONFIGS[name]
+
+
+def run_decode_ragged(args, g, dsa, gen, stream, cfg=None, name="decode_128k_ragged"):
     """The B=32 decode with sequence lengths uniform in [65536, 131072]
-    (seeded), two copies of the cache alternating so that reads come from
-    HBM, as in the main benchmark."""
+    (seeded), or the decode recipe `cfg`; two copies of the cache alternating
+    so that reads come from HBM, as in the main benchmark."""
     import torch
-    cfg = gen.ragged_decode_config()
+    cfg = cfg or gen.ragged_decode_config()
     B, Lmax, H, D, topk = cfg["B"], cfg["Lmax"], cfg["H"], cfg["D"], cfg["topk"]
     dd = [g.decode_inputs(cfg)]
     dd.append({k: (v.clone() if hasattr(v, "clone") else v) for k, v in dd[0].items()})
@@ -505,13 +524,13 @@ def run_decode_ragged(args, g, dsa, gen, stream):
     lens = gen.decode_lens(cfg)
     nbytes = decode_bytes(lens, H, D, topk, B)
     gbps = nbytes / (avg * 1e-3) / 1e9
-    return {"metric": METRIC, "workload": "decode_128k_ragged", "value": round(gbps, 1), "unit": "GB/s",
+    return {"metric": METRIC, "workload": name, "value": round(gbps, 1), "unit": "GB/s",
             "us_per_call": round(avg * 1e3, 2), "tokens": int(sum(int(n) for n in lens)),
             "rows_per_s": round(B / (avg * 1e-3), 1),
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                          "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None},
-            "config": {"workload": "decode_128k_ragged", "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
-                       "lens": "uniform in [Lmax/2, Lmax], seeded"}}
+            "config": {"workload": name, "B": B, "Lmax": Lmax, "H": H, "D": D, "topk": topk,
+                       "lens": "uniform in [Lmax/2, Lmax], seeded" if cfg.get("ragged") else "all Lmax"}}
 
 
 def run_prefill_ragged(args, g, dsa, gen, stream):
