@@ -846,9 +846,11 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
 
   // D. the candidates: entry i of the concatenation is entry i - base[w] of
   //    list w; the first gt_w of each list lie above bin d* and are selected
-  //    outright.  Entries tid + SL_NT j, j < SL_REG, are held in registers;
-  //    more (only with many equal scores) are read again when needed.
-  constexpr int SL_REG = 3;
+  //    outright.  Entries tid + SL_NT j, j < SL_REG, are held in registers
+  //    (5120: at k = 2048 the prefixes hold k plus the d* bin, up to about
+  //    4200 entries); more (a larger k, or many equal scores) are read again
+  //    from the lists at every pass over the candidates.
+  constexpr int SL_REG = 5;
   uint2 rc[SL_REG];
   bool ra[SL_REG];
 #pragma unroll
