@@ -649,7 +649,7 @@ struct SelShared {
   uint32_t fhist[FPC];                // its fine bins inside the boundary coarse bin
   uint32_t rhist[SL_NT];              // radix bins of the boundary-bin resolution
   uint32_t fw[DS_MAXWG][FPC];         // per list: those fine bins
-  int wtot[SL_NT / 64];
+  __attribute__((aligned(16))) int wtot[SL_NT / 64];
   int2 cut[DS_MAXWG];                 // per list: (lowest bin kept, entries)
   int gt[DS_MAXWG];                   // per list: entries above the boundary bin
   int base[DS_MAXWG + 1];             // list offsets in the concatenation of the prefixes read
@@ -664,11 +664,15 @@ __device__ int sl_scan(int v, SelShared& sh, int* total) {
   if (lane == 63) sh.wtot[wave] = incl;
   __syncthreads();
   int pre = 0, tot = 0;
+  static_assert(SL_NT % 256 == 0, "wave totals in 16-byte groups");
 #pragma unroll
-  for (int w = 0; w < SL_NT / 64; ++w) {
-    const int x = sh.wtot[w];
-    pre += (w < wave) ? x : 0;
-    tot += x;
+  for (int g = 0; g < SL_NT / 256; ++g) {
+    const v4i x4 = reinterpret_cast<const v4i*>(sh.wtot)[g];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pre += (4 * g + j < wave) ? x4[j] : 0;
+      tot += x4[j];
+    }
   }
   __syncthreads();
   *total = tot;
@@ -678,7 +682,7 @@ __device__ int sl_scan(int v, SelShared& sh, int* total) {
 }  // namespace
 
 __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, int nwg) {
-  extern __shared__ uint32_t dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   __shared__ SelShared sh;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -703,11 +707,12 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
   const int nchunk = (n + 31) >> 5;
   const int nact = min(nwg, (nchunk + DS_WAVES - 1) / DS_WAVES);
   const int nw = (n + 31) >> 5;
+  const int nw4 = (nw + 3) & ~3;       // bitmap words, rounded up to whole 16-byte groups (kept zero)
   uint32_t* bm = dyn;                  // selected keys
-  uint32_t* tb = dyn + nw;             // keys tied with the k-th, later word prefix counts
-  int* obuf = reinterpret_cast<int*>(dyn + 2 * nw);        // the output row, staged
-  float* osbuf = reinterpret_cast<float*>(dyn + 2 * nw + k);
-  for (int i = tid; i < nw; i += SL_NT) {
+  uint32_t* tb = dyn + nw4;            // keys tied with the k-th, later word prefix counts
+  int* obuf = reinterpret_cast<int*>(dyn + 2 * nw4);        // the output row, staged
+  float* osbuf = reinterpret_cast<float*>(dyn + 2 * nw4 + k);
+  for (int i = tid; i < nw4; i += SL_NT) {
     bm[i] = 0u;
     tb[i] = 0u;
   }
@@ -927,7 +932,13 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
   // F. ties with the k-th key: when more than need2 keys tie, the need2
   //    lowest indices (otherwise every tied key is taken)
   const int wpt = (nw + SL_NT - 1) / SL_NT;   // bitmap words per thread, contiguous
-  if (sh.ntie == need2) {             // uniform
+  // uniform: at most four words per thread, as one 16-byte group (thread t
+  // holds words 4t .. 4t + 3, those past nw are zero)
+  const bool w4 = nw4 <= 4 * SL_NT;
+  const bool g4 = 4 * tid < nw4;       // this thread's group exists
+  if (sh.ntie == need2 && w4) {
+    if (g4) reinterpret_cast<v4i*>(bm)[tid] |= reinterpret_cast<const v4i*>(tb)[tid];
+  } else if (sh.ntie == need2) {      // uniform
     for (int i = 0; i < wpt; ++i) {
       const int wd = tid * wpt + i;
       if (wd < nw) bm[wd] |= tb[wd];
@@ -956,7 +967,27 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
 
   // G. ascending output: the rank of a selected key is the number of
   //    selected keys below it (word prefix counts in tb, then a popcount)
-  {
+  if (w4) {
+    const v4i b4 = g4 ? reinterpret_cast<const v4i*>(bm)[tid] : v4i{0, 0, 0, 0};
+    const int c0 = __popc(b4[0]), c1 = __popc(b4[1]), c2 = __popc(b4[2]), c3 = __popc(b4[3]);
+    int t4;
+    const int pos = sl_scan(c0 + c1 + c2 + c3, sh, &t4);
+    if (!osc) {                        // uniform: indices straight from the bitmap
+      int q = pos;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t xw = (uint32_t)b4[i];
+        while (xw) {
+          const int bpos = __ffs(xw) - 1;
+          xw &= xw - 1;
+          if (q < k) out[q] = 32 * (4 * tid + i) + bpos;
+          ++q;
+        }
+      }
+      return;                          // exactly k bits are set: every position is written
+    }
+    if (g4) reinterpret_cast<v4i*>(tb)[tid] = v4i{pos, pos + c0, pos + c0 + c1, pos + c0 + c1 + c2};
+  } else {
     int c = 0;
     for (int i = 0; i < wpt; ++i) {
       const int wd = tid * wpt + i;
@@ -997,7 +1028,7 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
 static int score_workgroups(int Lmax) { return (Lmax + DS_KPB - 1) / DS_KPB; }
 
 size_t decode_select_lds_bytes(int Lmax, int topk) {
-  const size_t nw = ((size_t)Lmax + 31) / 32;
+  const size_t nw = (((size_t)Lmax + 31) / 32 + 3) & ~(size_t)3;   // bitmap words in whole 16-byte groups
   return (2 * nw + 2 * (size_t)topk) * sizeof(uint32_t);
 }
 
