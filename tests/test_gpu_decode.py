@@ -192,3 +192,25 @@ def test_decode_topk_one(dsa):
     note("decode topk=1")
     idx, sc = _run(dsa, inp, 1)
     _compare(idx, sc, inp, 1)
+
+
+def test_decode_bitmap_word_residues_with_and_without_scores(dsa):
+    """The select keeps its ascending-order bitmap in whole 16-byte groups of
+    four words and, without requested scores, writes the indices straight
+    from it.  Lengths whose word counts leave every residue mod 4 (and a
+    small tie at the k-th score, from repeated keys) run both output paths:
+    indices identical with and without scores, and against the oracle."""
+    import torch
+    Lmax, topk = 4100, 2048
+    lens = [2049, 2081, 2113, 2145, 4100, 4097, 3000, 2500]   # 65, 66, 67, 68, 129, 129, 94, 79 words
+    inp = _small_inputs(len(lens), Lmax, 64, 128, lens, seed=31)
+    inp["cache"][:, 1000:1040] = inp["cache"][:, 2000:2040]     # equal scores within each sequence
+    inp["k_scale"][:, 1000:1040] = inp["k_scale"][:, 2000:2040]
+    note("decode bitmap word residues, k=2048, with and without scores")
+    idx, sc = _run(dsa, inp, topk)
+    only, none = dsa.dsa_indexer_topk_decode(dev(inp["q"]), dev(inp["w"]), dev(inp["cache"]), dev(inp["k_scale"]),
+                                             dev(inp["lens"]), topk)
+    torch.cuda.synchronize()
+    assert none is None
+    assert np.array_equal(host(only), idx)
+    _compare(idx, sc, inp, topk)
