@@ -546,11 +546,6 @@ __global__ void __launch_bounds__(DS_NT, H > 64 ? 1 : 2) decode_score_kernel(Dec
       mine += (uint32_t)t[j];
     }
   }
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    reinterpret_cast<v4i*>(gh)[2 * tid + q] =
-        v4i{(int)(h16[8 * q] | (h16[8 * q + 1] << 16)), (int)(h16[8 * q + 2] | (h16[8 * q + 3] << 16)),
-            (int)(h16[8 * q + 4] | (h16[8 * q + 5] << 16)), (int)(h16[8 * q + 6] | (h16[8 * q + 7] << 16))};
   const uint32_t next_coarse = (uint32_t)__shfl_down((int)mine, 1);
   if ((tid & 1) == 0) gh[HBINS / 2 + tid / 2] = mine | (next_coarse << 16);
   // Its min(k, n) best keys and the rest of their boundary bin: a suffix sum
@@ -590,6 +585,15 @@ __global__ void __launch_bounds__(DS_NT, H > 64 ? 1 : 2) decode_score_kernel(Dec
         v4i{(int)first[4 * q], (int)first[4 * q + 1], (int)first[4 * q + 2], (int)first[4 * q + 3]};
   __syncthreads();
   const uint32_t dcut = (uint32_t)sh_cut[0];
+  // the fine bins go out only from the coarse bin of the cut up: the select
+  // never needs a list's fine counts below its cut (the bin of the
+  // sequence's k-th score is at or above every list's cut), and masks them
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (16u * tid + 15u >= dcut)
+      reinterpret_cast<v4i*>(gh)[2 * tid + q] =
+          v4i{(int)(h16[8 * q] | (h16[8 * q + 1] << 16)), (int)(h16[8 * q + 2] | (h16[8 * q + 3] << 16)),
+              (int)(h16[8 * q + 4] | (h16[8 * q + 5] << 16)), (int)(h16[8 * q + 6] | (h16[8 * q + 7] << 16))};
   // the workgroup's list: positions below DS_KCAP (positions count kept keys)
   const __amdgpu_buffer_rsrc_t crs = buf_rsrc(p.cand + ((size_t)b * nwg + x) * DS_KCAP, DS_KCAP * 8u);
   uint32_t* dummy = reinterpret_cast<uint32_t*>(ktr) + 64;   // per thread, past wsum
@@ -808,10 +812,13 @@ __global__ void __launch_bounds__(SL_NT) decode_select_kernel(DecodeParams p, in
     } else if (i < nact * (CBINS / 2 + FPC / 2)) {
       const int i2 = i - nact * (CBINS / 2);
       const int w = i2 / (FPC / 2), jj = i2 % (FPC / 2);
-      sh.fw[w][2 * jj] = t & 0xFFFFu;
-      sh.fw[w][2 * jj + 1] = t >> 16;
-      if (t & 0xFFFFu) atomicAdd(&sh.fhist[2 * jj], t & 0xFFFFu);
-      if (t >> 16) atomicAdd(&sh.fhist[2 * jj + 1], t >> 16);
+      // fine bins below the list's cut were not written (stale words): zero
+      const int lo = sh.cut[w].x - FPC * cstar;
+      const uint32_t f0 = 2 * jj >= lo ? (t & 0xFFFFu) : 0u, f1 = 2 * jj + 1 >= lo ? (t >> 16) : 0u;
+      sh.fw[w][2 * jj] = f0;
+      sh.fw[w][2 * jj + 1] = f1;
+      if (f0) atomicAdd(&sh.fhist[2 * jj], f0);
+      if (f1) atomicAdd(&sh.fhist[2 * jj + 1], f1);
     }
   }
   __syncthreads();
