@@ -26,8 +26,9 @@
 //    keys plus the rest of their boundary bin and writes them with their
 //    indices, grouped by bin from the highest: every key of the sequence's
 //    top k is among its workgroup's top k, so these lists hold the whole
-//    answer.  Its 16-bit histograms (4096 fine, 256 coarse bins) go out
-//    beside them.
+//    answer.  Its 16-bit histograms go out beside them: all 256 coarse
+//    bins, and the 4096 fine bins from the coarse bin of its cut up (the
+//    select reads none below a list's cut).
 // 2. decode_select_kernel, one workgroup per sequence: sums the coarse then
 //    the fine histograms of the sequence's workgroups to the bin of the k-th
 //    score, reads from every list only its prefix of bins at or above that
