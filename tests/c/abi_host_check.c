@@ -56,21 +56,25 @@ int main(void) {
   CHECK(dsa_indexer_topk_decode_workspace(32, 131072, 64, 128, 2048, &bytes) == DSA_OK && bytes > 0);
   CHECK(dsa_indexer_topk_prefill_varlen_workspace(4, 1000, 64, 128, 2048, DSA_FP8_E4M3, &bytes) == DSA_OK);
   CHECK(dsa_indexer_topk_decode_workspace(32, 131072, 12, 128, 2048, &bytes) == DSA_ERR_UNSUPPORTED);
+  CHECK(dsa_indexer_topk_decode_workspace(32, 131072, 136, 128, 2048, &bytes) == DSA_ERR_UNSUPPORTED);
   CHECK(standin_sparse_attention_workspace(0, 16, &bytes) == DSA_ERR_INVALID_ARG);
   /* workspace sizes across the supported range (the sanitizer build checks
      every layout on the way) */
   {
     static const int Ls[] = {1, 7, 2048, 32768, 196608};
-    static const int Hs[] = {8, 16, 32, 64};
+    static const int Hs[] = {8, 16, 32, 64, 128, 72};
     for (int a = 0; a < 5; ++a)
-      for (int h = 0; h < 4; ++h) {
+      for (int h = 0; h < 6; ++h) {
         CHECK(dsa_indexer_topk_prefill_workspace(Ls[a], Hs[h], 128, 2048, DSA_FP8_E4M3, &bytes) == DSA_OK && bytes > 0);
         CHECK(dsa_indexer_topk_prefill_workspace(Ls[a], Hs[h], 64, 1, DSA_BF16, &bytes) == DSA_OK && bytes > 0);
+        CHECK(dsa_indexer_topk_prefill_workspace(Ls[a], Hs[h], 128, 64, DSA_BF16, &bytes) == DSA_OK && bytes > 0);
       }
+    CHECK(dsa_indexer_topk_prefill_workspace(1024, 136, 128, 64, DSA_FP8_E4M3, &bytes) == DSA_ERR_UNSUPPORTED);
     static const int Lmaxs[] = {1, 31, 8192, 8193, 131072, 262144};
     for (int a = 0; a < 6; ++a) {
       CHECK(dsa_indexer_topk_decode_workspace(1, Lmaxs[a], 64, 128, 4096, &bytes) == DSA_OK && bytes > 0);
       CHECK(dsa_indexer_topk_decode_workspace(257, Lmaxs[a], 16, 64, 1, &bytes) == DSA_OK && bytes > 0);
+      CHECK(dsa_indexer_topk_decode_workspace(3, Lmaxs[a], 128, 128, 2048, &bytes) == DSA_OK && bytes > 0);
     }
     CHECK(dsa_indexer_topk_decode_workspace(1, 262145, 64, 128, 2048, &bytes) == DSA_ERR_UNSUPPORTED);
     CHECK(dsa_indexer_topk_prefill_varlen_workspace(1000, 2000000, 64, 128, 2048, DSA_FP8_E4M3, &bytes) == DSA_OK);
